@@ -1,0 +1,241 @@
+"""Pins of the oracle's store and attention against brute force, closed forms and invariants.
+
+No GPU. Each pin is chosen so that a plausible slip in the oracle (a wrong head map, a
+top-left causal mask, a dropped scale, a wrong gather index, a skipped padding check) fails
+at least one test; test_pins_catch_planted_mistakes shows that the brute-force comparison
+separates the planted variants from the right answer.
+"""
+import math
+from types import SimpleNamespace as NS
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import meta
+from paged_kv_cache_store_amd import workloads
+from helpers import bits, bf16_bits_to_f64, brute_attention, dense_kv
+
+
+def _tiny(seed, shape, n_prefill, n_decode, max_len, max_cached=0, pad_rows=0, share=False):
+    w = workloads.random_workload(seed, shape, n_prefill, n_decode, max_len=max_len,
+                                  max_cached=max_cached, pad_rows=pad_rows, share_prefix=share)
+    kc, vc, steps = workloads.materialize(w, "cpu")
+    return w, bits(kc).copy(), bits(vc).copy(), steps[0]
+
+
+def _run_prefill_oracle(w, kb, vb, st, step):
+    s = w.shape
+    m = meta.prepare_prefill(step.prefill, s.block_size)
+    scale = s.head_dim ** -0.5
+    out = oracle.attn_prefill(bits(st.q_prefill), kb, vb, m["cu_seqlens_q"], m["cu_seqlens_k"],
+                              m["block_tables"], s.num_heads, s.num_kv_heads, s.head_dim,
+                              s.block_size, scale)
+    return m, out
+
+
+SHAPES = [workloads.AttnShape(4, 2, 8, 4), workloads.AttnShape(4, 1, 8, 256),
+          workloads.AttnShape(6, 3, 128, 4), workloads.AttnShape(2, 2, 128, 256)]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"H{s.num_heads}/{s.num_kv_heads}d{s.head_dim}bs{s.block_size}")
+@pytest.mark.parametrize("seed", [1, 2])
+def test_prefill_matches_brute_force(oracle_lib, shape, seed):
+    w, kb, vb, st = _tiny(seed, shape, n_prefill=3, n_decode=0, max_len=40, max_cached=30)
+    step = w.steps[0]
+    m, out = _run_prefill_oracle(w, kb, vb, st, step)
+    q = bf16_bits_to_f64(bits(st.q_prefill))
+    scale = shape.head_dim ** -0.5
+    for b, s in enumerate(step.prefill):
+        q0, q1 = m["cu_seqlens_q"][b], m["cu_seqlens_q"][b + 1]
+        Lk = s.num_cached + s.num_new
+        K = dense_kv(kb, s.block_table, Lk, shape)
+        V = dense_kv(vb, s.block_table, Lk, shape)
+        ref = brute_attention(q[q0:q1], K, V, scale, offset=s.num_cached)
+        np.testing.assert_allclose(out[q0:q1], ref, atol=1e-12, rtol=0)
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"H{s.num_heads}/{s.num_kv_heads}d{s.head_dim}bs{s.block_size}")
+def test_decode_matches_brute_force(oracle_lib, shape):
+    w, kb, vb, st = _tiny(7, shape, n_prefill=0, n_decode=3, max_len=40, pad_rows=1)
+    step = w.steps[0]
+    m = meta.prepare_decode(step.decode, shape.block_size)
+    scale = shape.head_dim ** -0.5
+    out = oracle.attn_decode(bits(st.q_decode), kb, vb, m["context_lens"], m["block_tables"],
+                             shape.num_heads, shape.num_kv_heads, shape.head_dim,
+                             shape.block_size, scale)
+    q = bf16_bits_to_f64(bits(st.q_decode))
+    for b, s in enumerate(step.decode):
+        L = s.num_cached + s.num_new
+        if L == 0:
+            assert np.all(out[b] == 0.0)
+            continue
+        K = dense_kv(kb, s.block_table, L, shape)
+        V = dense_kv(vb, s.block_table, L, shape)
+        ref = brute_attention(q[b:b + 1], K, V, scale, offset=L - 1)
+        np.testing.assert_allclose(out[b:b + 1], ref, atol=1e-12, rtol=0)
+
+
+def test_pins_catch_planted_mistakes(oracle_lib):
+    """Each planted variant of the brute force must differ from the oracle by far more than
+    the tolerance, so the brute-force pin would catch the same slip in the oracle."""
+    shape = workloads.AttnShape(4, 2, 8, 4)
+    w, kb, vb, st = _tiny(3, shape, n_prefill=2, n_decode=0, max_len=12, max_cached=9)
+    step = w.steps[0]
+    m, out = _run_prefill_oracle(w, kb, vb, st, step)
+    q = bf16_bits_to_f64(bits(st.q_prefill))
+    scale = shape.head_dim ** -0.5
+    variants = dict(head_map=dict(head_map="strided"), align=dict(align="top_left"),
+                    scale=dict(drop_scale=True))
+    for name, kw in variants.items():
+        worst = 0.0
+        for b, s in enumerate(step.prefill):
+            q0, q1 = m["cu_seqlens_q"][b], m["cu_seqlens_q"][b + 1]
+            Lk = s.num_cached + s.num_new
+            K = dense_kv(kb, s.block_table, Lk, shape)
+            V = dense_kv(vb, s.block_table, Lk, shape)
+            bad = brute_attention(q[q0:q1], K, V, scale, offset=s.num_cached, **kw)
+            worst = max(worst, float(np.abs(bad - out[q0:q1]).max()))
+        assert worst > 0.05, name
+    # A wrong gather (block id used as the row offset instead of block id * block size).
+    s = step.prefill[0]
+    Lk = s.num_cached + s.num_new
+    K_good = dense_kv(kb, s.block_table, Lk, shape)
+    pool = bf16_bits_to_f64(kb).reshape(-1, shape.num_kv_heads, shape.head_dim)
+    K_bad = np.stack([pool[s.block_table[j // 4] + j % 4] for j in range(Lk)])
+    assert np.abs(K_bad - K_good).max() > 0.1
+
+
+def test_closed_forms(oracle_lib):
+    rng = np.random.default_rng(5)
+    d = 16
+    q = rng.standard_normal(d)
+    V = rng.standard_normal((9, d))
+    # All-zero keys: every weight is 1/n, the output is the mean of the values.
+    out, w = oracle.attend_row(q, np.zeros((9, d)), V, 0.25)
+    np.testing.assert_allclose(w, np.full(9, 1 / 9), atol=1e-15)
+    np.testing.assert_allclose(out, V.mean(axis=0), atol=1e-14)
+    # One key: weight exactly 1, output exactly that value.
+    out, w = oracle.attend_row(q, rng.standard_normal((1, d)), V[:1], 0.25)
+    assert w[0] == 1.0 and np.array_equal(out, V[0])
+    # Two keys: the weight of the first is the logistic function of the score gap.
+    K = rng.standard_normal((2, d))
+    out, w = oracle.attend_row(q, K, V[:2], 0.3)
+    gap = 0.3 * (q @ K[0] - q @ K[1])
+    assert abs(w[0] - 1 / (1 + math.exp(-gap))) < 1e-14
+    # Weights sum to one.
+    out, w = oracle.attend_row(q, rng.standard_normal((50, d)), rng.standard_normal((50, d)), 1.0)
+    assert abs(w.sum() - 1.0) < 1e-14
+    # No keys: zeros.
+    out, w = oracle.attend_row(q, np.zeros((0, d)), np.zeros((0, d)), 1.0)
+    assert np.all(out == 0)
+
+
+def test_argmax_probe_returns_exact_value(oracle_lib):
+    """A key aligned with q whose logit beats the rest by > 100 makes the output that key's
+    value exactly (exp(-100) vanishes against 1 in the sum)."""
+    shape = workloads.AttnShape(2, 1, 8, 4)
+    table = [5, 2, 7, 0]
+    L = 14
+    pool_k = np.zeros((8 * 4, 8), dtype=np.uint16)
+    pool_v = bits(torch.randn(8 * 4, 8).to(torch.bfloat16)).copy()
+    one = 0x3F80  # bf16 1.0
+    q = np.full((1, 2, 8), one, dtype=np.uint16)
+    for target in range(L):
+        pk = pool_k.copy()
+        row = meta.slot_of(table, target, 4)
+        pk[row, :] = 0x4200  # bf16 32.0 -> logit 32*8*scale = 90.5 vs 0 for the others
+        out = oracle.attn_decode(q, pk, pool_v, [L], np.array([table], np.int32), 2, 1, 8, 4,
+                                 8 ** -0.5 * 1.2)
+        expect = bf16_bits_to_f64(pool_v[row])
+        assert np.array_equal(out[0, 0], expect) and np.array_equal(out[0, 1], expect)
+
+
+def test_permutation_invariance(oracle_lib):
+    shape = workloads.AttnShape(4, 2, 8, 4)
+    w, kb, vb, st = _tiny(11, shape, n_prefill=3, n_decode=0, max_len=30, max_cached=20)
+    step = w.steps[0]
+    _, out = _run_prefill_oracle(w, kb, vb, st, step)
+    rng = np.random.default_rng(0)
+    perm = rng.permutation(w.num_blocks)  # new id of old block i is perm[i]
+    bs, D = shape.block_size, shape.row_elems
+    kp = np.empty_like(kb).reshape(w.num_blocks, bs * D)
+    vp = np.empty_like(vb).reshape(w.num_blocks, bs * D)
+    kp[perm] = kb.reshape(w.num_blocks, bs * D)
+    vp[perm] = vb.reshape(w.num_blocks, bs * D)
+    seqs = [NS(block_table=[int(perm[i]) for i in s.block_table], num_cached=s.num_cached,
+               num_new=s.num_new) for s in step.prefill]
+    m2 = meta.prepare_prefill(seqs, bs)
+    out2 = oracle.attn_prefill(bits(st.q_prefill), kp.reshape(kb.shape), vp.reshape(vb.shape),
+                               m2["cu_seqlens_q"], m2["cu_seqlens_k"], m2["block_tables"],
+                               shape.num_heads, shape.num_kv_heads, shape.head_dim, bs,
+                               shape.head_dim ** -0.5)
+    assert np.array_equal(out, out2)
+
+
+def test_decode_equals_last_prefill_row_and_chunks_equal_whole(oracle_lib):
+    shape = workloads.AttnShape(4, 2, 16, 4)
+    L = 23
+    table = [6, 1, 4, 0, 3, 5]
+    nb = 7
+    g = torch.Generator().manual_seed(3)
+    kc = bits(torch.randn(nb * 4, shape.row_elems, generator=g).to(torch.bfloat16)).copy()
+    vc = bits(torch.randn(nb * 4, shape.row_elems, generator=g).to(torch.bfloat16)).copy()
+    q = bits(torch.randn(L, shape.num_heads, shape.head_dim, generator=g).to(torch.bfloat16)).copy()
+    scale = shape.head_dim ** -0.5
+    args = (shape.num_heads, shape.num_kv_heads, shape.head_dim, 4, scale)
+
+    def prefill(cached, new):
+        m = meta.prepare_prefill([NS(block_table=table, num_cached=cached, num_new=new)], 4)
+        return oracle.attn_prefill(q[cached:cached + new], kc, vc, m["cu_seqlens_q"],
+                                   m["cu_seqlens_k"], m["block_tables"], *args)
+
+    whole = prefill(0, L)
+    # Chunked: positions [0, 9), [9, 17), [17, 23) give the same rows bit for bit.
+    parts = np.concatenate([prefill(0, 9), prefill(9, 8), prefill(17, 6)])
+    assert np.array_equal(parts, whole)
+    # Decode of the last token equals the last prefill row.
+    md = meta.prepare_decode([NS(block_table=table, num_cached=L - 1, num_new=1)], 4)
+    dec = oracle.attn_decode(q[L - 1:L], kc, vc, md["context_lens"], md["block_tables"], *args)
+    assert np.array_equal(dec[0], whole[-1])
+
+
+def test_gqa_equals_mha_with_repeated_kv_heads(oracle_lib):
+    shape = workloads.AttnShape(6, 2, 8, 4)
+    w, kb, vb, st = _tiny(13, shape, n_prefill=2, n_decode=0, max_len=20, max_cached=10)
+    step = w.steps[0]
+    m, out = _run_prefill_oracle(w, kb, vb, st, step)
+    G = 3
+    rep = lambda c: np.repeat(c.reshape(-1, 2, 8), G, axis=1).reshape(-1, 6 * 8).copy()
+    out_mha = oracle.attn_prefill(bits(st.q_prefill), rep(kb), rep(vb), m["cu_seqlens_q"],
+                                  m["cu_seqlens_k"], m["block_tables"], 6, 6, 8, 4, 8 ** -0.5)
+    assert np.array_equal(out, out_mha)
+
+
+def test_store_bit_copy_and_padding(oracle_lib):
+    shape = workloads.AttnShape(4, 2, 8, 4)
+    w, kb, vb, st = _tiny(17, shape, n_prefill=2, n_decode=3, max_len=10, max_cached=4,
+                          pad_rows=2)
+    step = w.steps[0]
+    sm = np.concatenate([meta.prepare_prefill(step.prefill, 4)["slot_mapping"],
+                         meta.prepare_decode(step.decode, 4)["slot_mapping"]])
+    assert (sm == -1).sum() == 2
+    qkv = bits(st.qkv).copy()
+    D = shape.row_elems
+    off_k = shape.num_heads * shape.head_dim
+    key = qkv[:, off_k:off_k + D]
+    value = qkv[:, off_k + D:]
+    k2, v2 = kb.copy(), vb.copy()
+    n = oracle.store_kvcache(key, value, k2, v2, sm)
+    assert n == (sm != -1).sum()
+    for i, s in enumerate(sm):
+        if s != -1:
+            assert np.array_equal(k2[s], key[i]) and np.array_equal(v2[s], value[i])
+    untouched = np.setdiff1d(np.arange(kb.shape[0]), sm[sm != -1])
+    assert np.array_equal(k2[untouched], kb[untouched])
+    assert np.array_equal(v2[untouched], vb[untouched])
+    # Storing the same rows again changes nothing.
+    k3, v3 = k2.copy(), v2.copy()
+    oracle.store_kvcache(key, value, k3, v3, sm)
+    assert np.array_equal(k3, k2) and np.array_equal(v3, v2)

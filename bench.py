@@ -1,0 +1,193 @@
+"""Benchmark of the paged-KV hot path on one MI355X.
+
+One step = the whole hot path over one batch: store every new K/V row, causal paged prefill,
+paged decode. Workload: the Qwen3-8B attention shape (32 q heads, 8 kv heads, head_dim 128,
+block size 256), 512 decode sequences with contexts uniform in 256..4096 plus a fresh 4 x
+1024-token prefill, blocks randomly permuted, N(0, 1) bf16 values. Inputs are resident in HBM
+before timing starts.
+
+Prints one JSON line. `value` is the decode attention's algorithmic HBM throughput (each
+visible K/V element once, plus q, out, tables and lengths) over its event-timed duration;
+prefill TFLOP/s and store GB/s are reported beside it, and the CPU oracle is timed on the host
+on the same step's decode.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixed_8b]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
+
+
+def decode_bytes(shape, context_lens) -> int:
+    L = np.asarray(context_lens, dtype=np.int64)
+    kv = int(L.sum()) * shape.num_kv_heads * shape.head_dim * 2 * 2
+    qo = 2 * len(L) * shape.num_heads * shape.head_dim * 2
+    tables = int(np.sum((L + shape.block_size - 1) // shape.block_size)) * 4 + len(L) * 4
+    return kv + qo + tables
+
+
+def prefill_flops(shape, seqs) -> int:
+    tot = 0
+    for s in seqs:
+        lq, p = s.num_new, s.num_cached
+        tot += shape.num_heads * 4 * shape.head_dim * (lq * p + lq * (lq + 1) // 2)
+    return tot
+
+
+def store_bytes(shape, slot_mapping) -> int:
+    sm = np.asarray(slot_mapping)
+    return int((sm != -1).sum()) * 4 * shape.row_elems * 2 + sm.size * 4
+
+
+def source_hash(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(kernel_src: str, per_launch_alg: float):
+    """HBM traffic of the decode kernel from the committed rocprofv3 counter summary, if it was
+    taken on the current source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "decode_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_sha256_16") != source_hash(kernel_src):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(shape, ds, k_cache, v_cache, scale):
+    """The oracle (as it stands) on the host cores: the whole decode step of the workload."""
+    import oracle  # test infrastructure: the baseline leg only
+    from oracle import meta
+    kb = k_cache.view(torch.int16).cpu().numpy().view(np.uint16)
+    vb = v_cache.view(torch.int16).cpu().numpy().view(np.uint16)
+    q = ds.tensors.q_decode.view(torch.int16).cpu().numpy().view(np.uint16)
+    m = meta.prepare_decode(ds.step.decode, shape.block_size)
+    t0 = time.perf_counter()
+    oracle.attn_decode(q, kb, vb, m["context_lens"], m["block_tables"], shape.num_heads,
+                       shape.num_kv_heads, shape.head_dim, shape.block_size, scale)
+    dt = time.perf_counter() - t0
+    nbytes = decode_bytes(shape, m["context_lens"])
+    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"whole decode step ({len(m['context_lens'])} sequences, "
+                      f"{nbytes / 1e9:.2f} GB of K/V) in fp64 C, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixed_8b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(this library has no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+
+    global torch
+    import torch
+    from paged_kv_cache_store_amd import step as gstep
+    from paged_kv_cache_store_amd import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = workloads.CONFIGS[args.workload]()
+    shape = w.shape
+    scale = shape.head_dim ** -0.5
+    k_cache, v_cache, tens = workloads.materialize(w, dev, poison=False)
+    dsteps = []
+    for st, t in zip(w.steps, tens):
+        ds = gstep.prepare_step(shape, st, t, dev)
+        ds.step = st
+        dsteps.append(ds)
+    torch.cuda.synchronize()
+
+    # Algorithmic work per step.
+    dec_bytes = sum(decode_bytes(shape, ds.host["decode"]["context_lens"])
+                    for ds in dsteps if "decode" in ds.host)
+    pre_flops = sum(prefill_flops(shape, st.prefill) for st in w.steps)
+    sto_bytes = sum(store_bytes(shape, ds.host["slot_mapping"]) for ds in dsteps)
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        for ds in dsteps:
+            gstep.run_step(ds, k_cache, v_cache, scale)
+    torch.cuda.synchronize()
+
+    names = ("store", "prefill", "decode")
+    ev = {n: [] for n in names}
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for ds in dsteps:
+            for n, fn in (("store", lambda: gstep.run_store(ds, k_cache, v_cache)),
+                          ("prefill", lambda: gstep.run_prefill(ds, k_cache, v_cache, scale)),
+                          ("decode", lambda: gstep.run_decode(ds, k_cache, v_cache, scale))):
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                fn()
+                b.record(stream)
+                ev[n].append((a, b))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = {n: sum(a.elapsed_time(b) for a, b in ev[n]) / args.steps for n in names}
+
+    dec_gbs = dec_bytes / (ms["decode"] * 1e-3) / 1e9 if dec_bytes else 0.0
+    pre_tflops = pre_flops / (ms["prefill"] * 1e-3) / 1e12 if pre_flops else 0.0
+    sto_gbs = sto_bytes / (ms["store"] * 1e-3) / 1e9
+    launches = max(1, sum(1 for ds in dsteps if "decode" in ds.host))
+    traffic = load_traffic(os.path.join(ROOT, "paged_kv_cache_store_amd", "csrc", "decode.hip"),
+                           dec_bytes / launches)
+
+    res = {
+        "metric": "paged decode attn HBM GB/s (% peak); prefill attn TFLOP/s (% bf16 MFMA)",
+        "value": round(dec_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 values, randomly permuted physical blocks)",
+        "config": {"workload": w.name, "num_heads": shape.num_heads,
+                   "num_kv_heads": shape.num_kv_heads, "head_dim": shape.head_dim,
+                   "block_size": shape.block_size, "decode_seqs": len(w.steps[0].decode),
+                   "prefill_tokens": w.steps[0].num_prefill_tokens, "seed": w.seed},
+        "parts": {
+            "store": {"ms": round(ms["store"], 4), "GB/s": round(sto_gbs, 1),
+                      "bytes": sto_bytes},
+            "prefill": {"ms": round(ms["prefill"], 4), "TFLOP/s": round(pre_tflops, 1),
+                        "frac_bf16_peak": round(pre_tflops / BF16_PEAK_TFLOPS, 4),
+                        "flops": pre_flops},
+            "decode": {"ms": round(ms["decode"], 4), "GB/s": round(dec_gbs, 1),
+                       "frac_hbm_peak": round(dec_gbs / HBM_PEAK_GBS, 4), "bytes": dec_bytes},
+        },
+        "roofline": {"bound": "hbm", "kernel": "decode (split partial + combine)",
+                     "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline and dsteps[0].context_lens is not None:
+        res["cpu_baseline"] = cpu_baseline(shape, dsteps[0], k_cache, v_cache, scale)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,164 @@
+"""CPU tests of the C ABI: the library loads and exports what include/nv_paged.h declares, the
+host metadata builder agrees bit for bit with the oracle's, and argument errors are reported
+before anything is launched. No call here reaches a kernel launch."""
+import ctypes
+import json
+import os
+import re
+from types import SimpleNamespace as NS
+
+import numpy as np
+import pytest
+
+from oracle import meta
+from paged_kv_cache_store_amd import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLD = json.load(open(os.path.join(ROOT, "tests", "golden", "worked_examples.json")))
+
+
+@pytest.fixture(scope="module")
+def nv():
+    from paged_kv_cache_store_amd import nvpaged
+    return nvpaged
+
+
+def test_exports_every_declared_symbol(nv):
+    header = open(os.path.join(ROOT, "include", "nv_paged.h")).read()
+    declared = set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(nv_\w+)\s*\(", header, re.M))
+    assert declared == set(nv.EXPORTS)
+    for name in declared:
+        assert hasattr(nv.lib(), name), name
+
+
+def test_status_strings(nv):
+    for code in (0, -1, -2, -3, -4):
+        assert nv.nv_status_string(code).startswith("NV_")
+    assert nv.nv_status_string(7) == "unknown nv_status"
+
+
+def _same_prefill(nv, seqs, bs):
+    a = nv.nv_prepare_prefill(seqs, bs)
+    b = meta.prepare_prefill(seqs, bs)
+    for k in ("slot_mapping", "cu_seqlens_q", "cu_seqlens_k"):
+        assert np.array_equal(a[k], b[k]), k
+    assert a["max_seqlen_q"] == b["max_seqlen_q"] and a["max_seqlen_k"] == b["max_seqlen_k"]
+    assert a["has_cached_context"] == b["has_cached_context"]
+    w = b["block_tables"].shape[1]
+    assert np.array_equal(a["block_tables"][:, :w], b["block_tables"])
+
+
+def _same_decode(nv, seqs, bs):
+    a = nv.nv_prepare_decode(seqs, bs)
+    b = meta.prepare_decode(seqs, bs)
+    for k in ("slot_mapping", "context_lens"):
+        assert np.array_equal(a[k], b[k]), k
+    w = b["block_tables"].shape[1]
+    if w:
+        assert np.array_equal(a["block_tables"][:, :w], b["block_tables"])
+    else:
+        assert np.all(a["block_tables"] == -1)
+
+
+def test_metadata_worked_examples(nv):
+    g = GOLD["prefill_packing"]
+    seqs = [NS(**{k: v for k, v in s.items() if k != "name"}) for s in g["seqs"]]
+    p = nv.nv_prepare_prefill(seqs, g["block_size"])
+    assert p["slot_mapping"].tolist() == g["slot_mapping"]
+    assert p["cu_seqlens_k"].tolist() == g["cu_seqlens_k"]
+    assert p["has_cached_context"] is True
+    g = GOLD["decode_counters"]
+    d = nv.nv_prepare_decode([NS(block_table=g["block_table"], num_cached=g["num_tokens"] - 1,
+                                 num_new=1)], g["block_size"])
+    assert d["slot_mapping"].tolist() == g["slot_mapping"]
+    assert d["context_lens"].tolist() == g["context_lens"]
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("bs", [4, 16, 48, 256])
+def test_metadata_matches_oracle_random(nv, seed, bs):
+    shape = workloads.AttnShape(4, 2, 128, bs)
+    w = workloads.random_workload(seed, shape, n_prefill=5, n_decode=7, max_len=600,
+                                  max_cached=500, pad_rows=2, share_prefix=seed % 2 == 1)
+    st = w.steps[0]
+    _same_prefill(nv, st.prefill, bs)
+    _same_decode(nv, st.decode, bs)
+
+
+@pytest.mark.parametrize("name", list(workloads.CONFIGS))
+def test_metadata_matches_oracle_configs(nv, name):
+    w = workloads.CONFIGS[name]()
+    for st in w.steps:
+        if st.prefill:
+            _same_prefill(nv, st.prefill, w.shape.block_size)
+        if st.decode:
+            _same_decode(nv, st.decode, w.shape.block_size)
+
+
+def test_metadata_rejects_bad_tables(nv):
+    with pytest.raises(nv.NvError):
+        nv.nv_prepare_prefill([NS(block_table=[0], num_cached=0, num_new=5)], 4)
+    with pytest.raises(nv.NvError):
+        nv.nv_prepare_decode([NS(block_table=[0], num_cached=3, num_new=2)], 4)
+    with pytest.raises(nv.NvError):  # table longer than the sequence needs
+        nv.nv_prepare_decode([NS(block_table=[0, 1], num_cached=2, num_new=1)], 4)
+
+
+def test_check_indices(nv):
+    ok, _ = nv.nv_check_indices(np.array([3, -1, 7], np.int32), 8,
+                                np.array([[0, 1], [1, -1]], np.int32), np.array([8, 3], np.int32),
+                                4, 2)
+    assert ok
+    ok, bad = nv.nv_check_indices(np.array([3, 3], np.int32), 8, np.zeros((0, 0), np.int32),
+                                  np.zeros(0, np.int32), 4, 2)
+    assert not ok and bad == 1  # duplicate slot
+    ok, bad = nv.nv_check_indices(np.array([9], np.int32), 8, np.zeros((0, 0), np.int32),
+                                  np.zeros(0, np.int32), 4, 2)
+    assert not ok and bad == 0  # slot outside the pool
+    ok, bad = nv.nv_check_indices(np.zeros(0, np.int32), 8, np.array([[0, -1]], np.int32),
+                                  np.array([5], np.int32), 4, 2)
+    assert not ok and bad == 1  # padding entry inside the read range
+
+
+def test_device_calls_reject_bad_arguments_without_launch(nv):
+    L = nv.lib()
+    null = None
+    # store: null pointers, short row stride
+    assert L.nv_store_kvcache(null, 1024, null, 1024, null, null, null, 4, 8, 128, 16, null) == -1
+    assert L.nv_store_kvcache(1, 512, 1, 1024, 1, 1, 1, 4, 8, 128, 16, null) == -1
+    assert L.nv_store_kvcache(null, 1024, null, 1024, null, null, null, 0, 8, 128, 16, null) == 0
+    # prefill: q heads not a multiple of kv heads; head_dim 64 unsupported; no block table
+    args = [1, 1, 1, 1, 1, 8, 8, 1, 1, 1]
+    assert L.nv_paged_attn_prefill(*args, 6, 4, 128, 256, 0.1, 1, null) == -1
+    assert L.nv_paged_attn_prefill(*args, 8, 4, 64, 256, 0.1, 1, null) == -2
+    assert L.nv_paged_attn_prefill(1, 1, 1, 1, 1, 8, 8, null, 1, 1, 8, 4, 128, 256, 0.1, 1,
+                                   null) == -2
+    assert L.nv_paged_attn_prefill(1, 1, 1, 1, 1, 9, 8, 1, 1, 1, 8, 4, 128, 256, 0.1, 1,
+                                   null) == -1  # max_seqlen_q > max_seqlen_k
+    assert L.nv_paged_attn_prefill(1, 1, 1, 1, 1, 8, 300, 1, 1, 1, 8, 4, 128, 256, 0.1, 1,
+                                   null) == -1  # keys beyond the table width
+    # decode: workspace too small
+    need = nv.nv_paged_attn_decode_workspace_size(4, 16, 8, 128, 3, 256)
+    assert need > 0
+    assert L.nv_paged_attn_decode(1, 1, 1, 1, 1, 3, 4, 16, 8, 128, 256, 0.1, 256, need - 1, 1,
+                                  null) == -4
+    assert L.nv_paged_attn_decode(1, 1, 1, 1, 1, 3, 4, 16, 8, 128, 256, 0.1, null, need, 1,
+                                  null) == -4
+    assert L.nv_paged_attn_decode(1, 1, 1, 1, 1, 3, 4, 16, 8, 64, 256, 0.1, 256, need, 1,
+                                  null) == -2
+    assert L.nv_paged_attn_decode(1, 1, 1, 1, 1, 3, 4, 48, 4, 128, 256, 0.1, 256, need, 1,
+                                  null) == -2  # group of 12 q heads per kv head
+    assert L.nv_paged_attn_decode(null, 1, 1, 1, 1, 3, 0, 16, 8, 128, 256, 0.1, null, 0, null,
+                                  null) == 0  # empty batch
+
+
+def test_decode_split_choice(nv):
+    # Small batches get short splits so the chip fills; large ones get 512-key splits.
+    assert nv.nv_paged_attn_decode_split_keys(6, 8, 3, 256) == 64
+    assert nv.nv_paged_attn_decode_split_keys(256, 8, 16, 256) == 512
+    assert nv.nv_paged_attn_decode_split_keys(512, 8, 16, 256) == 512
+    for b in (1, 3, 17, 100, 600):
+        s = nv.nv_paged_attn_decode_split_keys(b, 8, 16, 256)
+        assert s % 64 == 0 and 64 <= s <= 512
+    # One split covers every context: no workspace needed.
+    assert nv.nv_paged_attn_decode_workspace_size(4096, 16, 8, 128, 1, 256) == 0

@@ -1,0 +1,129 @@
+"""GPU parity: the HIP library against the oracle on the same seeded inputs.
+
+Store and indexing: bit-exact over the whole pool (untouched rows included). Attention: max
+abs error <= 1e-2 (see gpu_common.attn_bound for the |o| >= 4 rounding allowance) and mean abs
+error <= 1e-3. Unowned blocks hold NaN, so a read outside a sequence's table fails loudly.
+Full-size configurations are checked on sampled sequences the oracle computes one by one, plus
+finiteness of every output.
+"""
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_store_amd import workloads
+from gpu_common import Run, assert_attn_close, check_metadata, check_pools_bit_exact
+
+pytestmark = pytest.mark.gpu
+
+
+def _full_check(w, label):
+    run = Run(w)
+    stats = {}
+    for i, st in enumerate(w.steps):
+        print(f"[{label}] step {i}: {len(st.prefill)} prefill seqs, {len(st.decode)} decode rows",
+              flush=True)
+        ds = run.gpu_step(i)
+        om = run.oracle_store(i)
+        check_metadata(ds, om)
+        check_pools_bit_exact(run, f"{label} step {i}")
+        if st.prefill:
+            rows, ref = run.oracle_prefill(i, om)
+            stats[f"prefill{i}"] = assert_attn_close(ds.out_prefill[rows], ref,
+                                                     f"{label} prefill step {i}")
+        if st.decode:
+            ids, ref = run.oracle_decode(i)
+            stats[f"decode{i}"] = assert_attn_close(ds.out_decode[ids], ref,
+                                                    f"{label} decode step {i}")
+    return stats
+
+
+def test_config_decode_small():
+    print(_full_check(workloads.config_decode_small(), "decode_small"))
+
+
+def test_config_prefill_varlen():
+    print(_full_check(workloads.config_prefill_varlen(), "prefill_varlen"))
+
+
+SHAPES = [workloads.AttnShape(16, 8, 128, 256), workloads.AttnShape(32, 8, 128, 256),
+          workloads.AttnShape(8, 8, 128, 64), workloads.AttnShape(12, 4, 128, 48),
+          workloads.AttnShape(16, 2, 128, 16), workloads.AttnShape(8, 4, 128, 512),
+          workloads.AttnShape(10, 2, 128, 128)]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"{s.num_heads}q{s.num_kv_heads}kv_bs{s.block_size}")
+@pytest.mark.parametrize("seed", [0, 1])
+def test_random_mixed(shape, seed):
+    w = workloads.random_workload(100 + seed, shape, n_prefill=4, n_decode=9, max_len=700,
+                                  max_cached=600, pad_rows=2, share_prefix=seed == 1)
+    print(_full_check(w, f"random {shape} seed {seed}"))
+
+
+def test_edge_lengths():
+    """Lengths around tile and block edges: 1, 63, 64, 65, 255, 256, 257 new tokens and
+    single-key decode rows."""
+    shape = workloads.AttnShape(16, 8, 128, 256)
+    lens = [1, 63, 64, 65, 255, 256, 257, 129]
+    cached = [0, 1, 64, 191, 0, 256, 255, 1]
+    rng = np.random.default_rng(9)
+    need = sum(-(-(c + n) // 256) for c, n in zip(cached, lens)) + 4 + 2
+    pool = workloads._Pool(need, rng)
+    pre = [workloads.Seq(pool.take(-(-(c + n) // 256)), c, n) for c, n in zip(cached, lens)]
+    dec = [workloads.Seq(pool.take(1), 0, 1), workloads.Seq(pool.take(1), 255, 1),
+           workloads.Seq(pool.take(2), 256, 1), workloads.Seq([], 0, 0)]
+    w = workloads.Workload("edges", shape, need, pool.owned,
+                           [workloads.Step(prefill=pre, decode=dec)], 9)
+    print(_full_check(w, "edges"))
+
+
+def test_all_padding_decode_rows():
+    shape = workloads.AttnShape(16, 8, 128, 256)
+    w = workloads.Workload("pad", shape, 2, np.zeros(2, bool),
+                           [workloads.Step(decode=[workloads.Seq([], 0, 0)] * 3)], 5)
+    run = Run(w)
+    ds = run.gpu_step(0)
+    assert torch.count_nonzero(ds.out_decode).item() == 0
+    om = run.oracle_store(0)
+    check_pools_bit_exact(run, "padding rows store nothing")
+
+
+def _sampled_check(w, label, prefill_ids=None, decode_ids=None):
+    run = Run(w)
+    stats = {}
+    for i, st in enumerate(w.steps):
+        print(f"[{label}] step {i}", flush=True)
+        ds = run.gpu_step(i)
+        om = run.oracle_store(i)
+        check_metadata(ds, om)
+        check_pools_bit_exact(run, f"{label} step {i}")
+        if st.prefill:
+            assert torch.isfinite(ds.out_prefill.float()).all()
+            rows, ref = run.oracle_prefill(i, om, prefill_ids)
+            stats[f"prefill{i}"] = assert_attn_close(ds.out_prefill[rows], ref,
+                                                     f"{label} prefill step {i}")
+        if st.decode:
+            assert torch.isfinite(ds.out_decode.float()).all()
+            ids, ref = run.oracle_decode(i, decode_ids)
+            stats[f"decode{i}"] = assert_attn_close(ds.out_decode[ids], ref,
+                                                    f"{label} decode step {i}")
+    return stats
+
+
+def test_config_prefix_chunked_sampled():
+    # One prompt from each prefix group, both chunks.
+    print(_sampled_check(workloads.config_prefix_chunked(), "prefix_chunked",
+                         prefill_ids=[0, 5, 10, 15]))
+
+
+def test_config_decode_large_sampled():
+    w = workloads.config_decode_large()
+    lens = np.array([s.num_cached + 1 for s in w.steps[0].decode])
+    ids = sorted(set([int(lens.argmax()), int(lens.argmin())] +
+                     list(np.random.default_rng(0).choice(len(lens), 14, replace=False))))
+    print(_sampled_check(w, "decode_large", decode_ids=ids))
+
+
+def test_config_mixed_8b_sampled():
+    w = workloads.config_mixed_8b()
+    ids = sorted(np.random.default_rng(1).choice(512, 12, replace=False).tolist())
+    print(_sampled_check(w, "mixed_8b", prefill_ids=[0, 3], decode_ids=ids))

@@ -20,8 +20,6 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python __graft_entry__.py build` "
                       "(or paged_kv_cache_store_amd/build.py) before using the HIP path")
 
-_lib = ctypes.CDLL(LIB_PATH)
-
 EXPORTS = ("nv_status_string", "nv_store_kvcache", "nv_paged_attn_prefill",
            "nv_paged_attn_decode_workspace_size", "nv_paged_attn_decode",
            "nv_paged_attn_decode_split_keys", "nv_prepare_prefill", "nv_prepare_decode",
@@ -29,26 +27,36 @@ EXPORTS = ("nv_status_string", "nv_store_kvcache", "nv_paged_attn_prefill",
 
 _p, _i32, _i64, _f32, _sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
                               ctypes.c_size_t)
-_lib.nv_status_string.argtypes = [ctypes.c_int]
-_lib.nv_status_string.restype = ctypes.c_char_p
-_lib.nv_store_kvcache.argtypes = [_p, _i64, _p, _i64, _p, _p, _p, _i64, _i32, _i32, _i64, _p]
-_lib.nv_store_kvcache.restype = ctypes.c_int
-_lib.nv_paged_attn_prefill.argtypes = [_p, _p, _p, _p, _p, _i32, _i32, _p, _i32, _i32, _i32,
-                                       _i32, _i32, _i32, _f32, _p, _p]
-_lib.nv_paged_attn_prefill.restype = ctypes.c_int
-_lib.nv_paged_attn_decode_workspace_size.argtypes = [_i32] * 6
-_lib.nv_paged_attn_decode_workspace_size.restype = _sz
-_lib.nv_paged_attn_decode_split_keys.argtypes = [_i32] * 4
-_lib.nv_paged_attn_decode_split_keys.restype = _i32
-_lib.nv_paged_attn_decode.argtypes = [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
-                                      _f32, _p, _sz, _p, _p]
-_lib.nv_paged_attn_decode.restype = ctypes.c_int
-_lib.nv_prepare_prefill.argtypes = [_p, _p, _p, _p, _i32, _i32, _p, _p, _p, _p, _p, _p, _i32, _p]
-_lib.nv_prepare_prefill.restype = ctypes.c_int
-_lib.nv_prepare_decode.argtypes = [_p, _p, _p, _p, _i32, _i32, _p, _p, _p, _i32]
-_lib.nv_prepare_decode.restype = ctypes.c_int
-_lib.nv_check_indices.argtypes = [_p, _i64, _i64, _p, _p, _i32, _i32, _i32, _i64, _p]
-_lib.nv_check_indices.restype = ctypes.c_int
+
+
+def _bind(path: str) -> ctypes.CDLL:
+    """Loads a build of the library and declares the C signatures of its entry points."""
+    L = ctypes.CDLL(path)
+    L.nv_status_string.argtypes = [ctypes.c_int]
+    L.nv_status_string.restype = ctypes.c_char_p
+    L.nv_store_kvcache.argtypes = [_p, _i64, _p, _i64, _p, _p, _p, _i64, _i32, _i32, _i64, _p]
+    L.nv_store_kvcache.restype = ctypes.c_int
+    L.nv_paged_attn_prefill.argtypes = [_p, _p, _p, _p, _p, _i32, _i32, _p, _i32, _i32, _i32,
+                                        _i32, _i32, _i32, _f32, _p, _p]
+    L.nv_paged_attn_prefill.restype = ctypes.c_int
+    L.nv_paged_attn_decode_workspace_size.argtypes = [_i32] * 6
+    L.nv_paged_attn_decode_workspace_size.restype = _sz
+    L.nv_paged_attn_decode_split_keys.argtypes = [_i32] * 4
+    L.nv_paged_attn_decode_split_keys.restype = _i32
+    L.nv_paged_attn_decode.argtypes = [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
+                                       _f32, _p, _sz, _p, _p]
+    L.nv_paged_attn_decode.restype = ctypes.c_int
+    L.nv_prepare_prefill.argtypes = [_p, _p, _p, _p, _i32, _i32, _p, _p, _p, _p, _p, _p, _i32,
+                                     _p]
+    L.nv_prepare_prefill.restype = ctypes.c_int
+    L.nv_prepare_decode.argtypes = [_p, _p, _p, _p, _i32, _i32, _p, _p, _p, _i32]
+    L.nv_prepare_decode.restype = ctypes.c_int
+    L.nv_check_indices.argtypes = [_p, _i64, _i64, _p, _p, _i32, _i32, _i32, _i64, _p]
+    L.nv_check_indices.restype = ctypes.c_int
+    return L
+
+
+_lib = _bind(LIB_PATH)
 
 NV_OK, NV_ERR_INVALID_ARG, NV_ERR_UNSUPPORTED, NV_ERR_LAUNCH, NV_ERR_WORKSPACE = 0, -1, -2, -3, -4
 

@@ -99,7 +99,7 @@ nv_status nv_store_kvcache(const void *key, int64_t key_row_stride,
  *   max_seqlen_q   host int >= every Lq_b: sizes the launch without a device round trip.
  *   max_seqlen_k   host int >= every Lk_b.
  *   block_tables   device int32 [batch, max_blocks_per_seq].
- *   softmax_scale  the engine passes head_dim ** -0.5.
+ *   softmax_scale  positive and finite; the engine passes head_dim ** -0.5.
  *   out            device bf16 [total_q, num_heads, head_dim] contiguous; may not alias q.
  * Supported: head_dim == 128, num_heads % num_kv_heads == 0, (num_heads / num_kv_heads) <= 8,
  * block_size >= 1. block_tables == NULL (the packed fresh-K/V mode of the engine's first
@@ -130,6 +130,7 @@ nv_status nv_paged_attn_prefill(const void *q, const void *k_cache, const void *
  *                 256-byte aligned, owned by the caller; its contents need no initialisation
  *                 and are garbage afterwards. Calls that run concurrently need separate
  *                 workspaces. May be NULL when the required size is 0.
+ *   softmax_scale positive and finite; the engine passes head_dim ** -0.5.
  *   out           device bf16 [batch, num_heads, head_dim] contiguous.
  * Supported: head_dim == 128, num_heads % num_kv_heads == 0, (num_heads / num_kv_heads) <= 8,
  * block_size >= 1.

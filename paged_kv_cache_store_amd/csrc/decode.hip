@@ -5,28 +5,51 @@
 // context_lens[b] keys of sequence b, read through its block table. Query head h reads kv head
 // h / G (G = num_heads / num_kv_heads). A row with no keys (a padding row) outputs zeros.
 //
-// gfx950 design. Decode reads every K/V byte of the context once and does ~1 FMA per byte, so
-// it is bound by HBM bandwidth. Work item = (sequence b, kv head g, split s of the key range);
-// the G query heads of the group share every K/V load. A workgroup of 4 waves
-//   1) streams the split's keys of kv head g: 16 lanes x 16 B cover one 256-byte key row, a
-//      wave covers 4 keys per load; partial dot products are summed across the 16 lanes with
-//      DPP row rotations and the scores (already in log2 units) go to LDS;
-//   2) takes the exact max and sum of exp2 over the split's scores (no running rescale);
-//   3) streams the same keys' values, each lane accumulating 8 output dims for all G heads,
-//      then reduces over keys with two cross-lane swaps and an LDS sum over the 4 waves.
-// A split's result is final when it is the sequence's only split; otherwise (max, sum,
-// unnormalised output) goes to the workspace and a second kernel merges the splits with the
-// log-sum-exp rule: out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, M = max_s m_s.
-// The split size depends only on host-known launch parameters, so there is no device round
-// trip.
+// gfx950 design. Decode reads every K/V byte of the context once and does ~1 FMA per byte: it
+// is bound by HBM bandwidth, so the kernel is built around keeping enough bytes in flight and
+// spending few instructions per byte.
+//  - Work item = (sequence b, kv head g, split s of the key range). The G query heads of the
+//    group share every K/V load. The split's slice of the block table is staged in LDS once,
+//    so no K/V address waits on a table load.
+//  - Each of the 4 waves of a workgroup walks its own chunks of 32 keys (chunks w, w+4, ...)
+//    with an online softmax. K and V of the next chunk are loaded while the current one is
+//    processed (two register buffers), 16 KiB per wave in flight.
+//  - Lane layout: 16 lanes x 16 B cover one 256-byte key (or value) row of the kv head, a wave
+//    covers 4 rows per load instruction. K . q is v_dot2_f32_bf16 (bf16 pairs, fp32 sum)
+//    followed by a DPP sum over the 16 lanes of the row; P.V is fp32 FMA with 8 output dims per
+//    lane. (Scores by a 16x16x32 bf16 MFMA with the query heads as columns were measured
+//    slower: the extra registers halve the waves per SIMD.)
+//  - At the end the 4 waves' (max, sum, output) are merged through LDS. A split's result is
+//    final when it is the sequence's only split; otherwise it goes to the workspace and a
+//    second kernel merges the splits with the log-sum-exp rule:
+//    out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, M = max_s m_s.
+//  - Scores are kept in log2 units (scale * log2(e) folded in; exp2 is the hardware exp).
+// The split size depends only on host-known launch parameters: no device round trip.
 #include "nv_common.h"
+
+// Build-time knobs (defaults are the measured best on MI355X).
+#ifndef NV_DECODE_NT
+#define NV_DECODE_NT 1          // non-temporal K/V loads
+#endif
+#ifndef NV_DECODE_CHUNK
+#define NV_DECODE_CHUNK 16      // keys per wave iteration (16 or 32)
+#endif
+#ifndef NV_DECODE_TARGET_ITEMS
+#define NV_DECODE_TARGET_ITEMS 4096  // work items the split size aims for
+#endif
+#ifndef NV_DECODE_MIN_WAVES
+#define NV_DECODE_MIN_WAVES 1   // occupancy hint: waves per SIMD the register budget must allow
+#endif
 
 namespace nvp {
 namespace {
 
-constexpr int kMaxSplitKeys = 512;
-constexpr int kMinSplitKeys = 64;
-constexpr int kUnroll = 8;  // 16-byte loads in flight per lane per phase
+static_assert(NV_DECODE_CHUNK == 16 || NV_DECODE_CHUNK == 32, "chunk of 16 or 32 keys");
+constexpr int kChunk = NV_DECODE_CHUNK;  // keys per wave iteration
+constexpr int kRowLoads = kChunk / 4;    // 16-byte loads per lane per chunk, per tensor
+constexpr int kMaxSplitKeys = 2048;
+constexpr int kMinSplitKeys = 128;
+constexpr int kTableSlots = 264;    // block ids of one split staged in LDS
 
 struct DecodeArgs {
     const uint16_t *q;
@@ -47,11 +70,28 @@ struct DecodeArgs {
     float scale_log2;  // softmax_scale * log2(e)
 };
 
+struct Chunk {
+    u32x4 k[kRowLoads];
+    u32x4 v[kRowLoads];
+};
+
+// Streaming 16-byte load of K/V (non-temporal by default: each byte is read once).
+#if NV_DECODE_NT
+#define NV_LOAD_STREAM(ptr) __builtin_nontemporal_load(ptr)
+#else
+#define NV_LOAD_STREAM(ptr) (*(ptr))
+#endif
+
 template <int G>
-__global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
-    __shared__ float sc[G][kMaxSplitKeys];
-    __shared__ float red[4][G][kHeadDim];
-    __shared__ float stat[4][G];
+struct DecodeSmem {
+    int32_t table[kTableSlots];
+    float o[4][G][kHeadDim];
+    float ml[4][G][2];
+};
+
+template <int G>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NV_DECODE_MIN_WAVES))) void decode_split_kernel(DecodeArgs a) {
+    __shared__ DecodeSmem<G> sm;
 
     const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int L = a.context_lens[b];
@@ -61,160 +101,195 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
     const int nsplit = (L + a.split_keys - 1) / a.split_keys;
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-    const int sub = lane >> 4;  // which of the wave's 4 keys
-    const int c = lane & 15;    // dims [8c, 8c + 8)
-    const int Hkv = a.num_kv_heads;
-    const int32_t *table = a.block_tables + (int64_t)b * a.bt_width;
+    const int bs = a.block_size;
+    const int lb0 = a.bs_shift >= 0 ? (k0 >> a.bs_shift) : k0 / bs;
+    {
+        const int lb1 = a.bs_shift >= 0 ? ((k0 + n - 1) >> a.bs_shift) : (k0 + n - 1) / bs;
+        const int32_t *table = a.block_tables + (int64_t)b * a.bt_width;
+        for (int i = tid; i <= lb1 - lb0; i += 256) sm.table[i] = table[lb0 + i];
+    }
+    // Pool row of key k0 + jl.
+    auto row_of = [&](int jl) -> int64_t {
+        const int j = k0 + jl;
+        int lb, off;
+        if (a.bs_shift >= 0) {
+            lb = j >> a.bs_shift;
+            off = j & (bs - 1);
+        } else {
+            lb = j / bs;
+            off = j - lb * bs;
+        }
+        return (int64_t)sm.table[lb - lb0] * bs + off;
+    };
 
-    // q of the G heads, 8 dims per lane, pre-scaled into log2 units.
-    float qf[G][8];
+    const int64_t rs = (int64_t)a.num_kv_heads * kHeadDim;  // pool row stride (elements)
+    const uint16_t *kbase = a.k_cache + (int64_t)g * kHeadDim;
+    const uint16_t *vbase = a.v_cache + (int64_t)g * kHeadDim;
+    const uint16_t *qbase = a.q + ((int64_t)b * a.num_heads + g * G) * kHeadDim;
+    const int sub = lane >> 4;  // key slot of the 16-lane row
+    const int dc = lane & 15;   // dims [8 dc, 8 dc + 8) in the row layout
+
+    // This lane's 8 dims of every query head of the group, as bf16 pairs.
+    uint32_t qp[G][4];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(
-            a.q + ((int64_t)b * a.num_heads + g * G + h) * kHeadDim + 8 * c);
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(qbase + h * kHeadDim + 8 * dc);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            qf[h][2 * i] = bf16lo(v[i]) * a.scale_log2;
-            qf[h][2 * i + 1] = bf16hi(v[i]) * a.scale_log2;
-        }
+        for (int i = 0; i < 4; ++i) qp[h][i] = v[i];
     }
+    __syncthreads();  // table slice visible
 
-    const uint16_t *kbase = a.k_cache + (int64_t)g * kHeadDim + 8 * c;
-    const uint16_t *vbase = a.v_cache + (int64_t)g * kHeadDim + 8 * c;
-    const int64_t row_stride = (int64_t)Hkv * kHeadDim;
-
-    // Phase 1: scores.
-    for (int base = 0; base < n; base += 16 * kUnroll) {
-        u32x4 kv[kUnroll];
+    auto load_chunk = [&](Chunk &buf, int ch) {
+        const int kc = ch * kChunk;
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int kk = base + 16 * u + 4 * w + sub;
-            if (kk < n) {
-                const int64_t row = key_row(table, k0 + kk, a.block_size, a.bs_shift);
-                kv[u] = __builtin_nontemporal_load(
-                    reinterpret_cast<const u32x4 *>(kbase + row * row_stride));
-            } else {
-                kv[u] = u32x4{0, 0, 0, 0};
-            }
+        for (int i = 0; i < kRowLoads; ++i) {
+            const int jl = kc + 4 * i + sub;
+            const bool ok = jl < n;
+            const int64_t off = (ok ? row_of(jl) : 0) * rs + 8 * dc;
+            buf.k[i] = ok ? NV_LOAD_STREAM(reinterpret_cast<const u32x4 *>(kbase + off))
+                          : u32x4{0, 0, 0, 0};
+            buf.v[i] = ok ? NV_LOAD_STREAM(reinterpret_cast<const u32x4 *>(vbase + off))
+                          : u32x4{0, 0, 0, 0};
         }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int kk = base + 16 * u + 4 * w + sub;
-            float kf[8];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                kf[2 * i] = bf16lo(kv[u][i]);
-                kf[2 * i + 1] = bf16hi(kv[u][i]);
-            }
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-                float d = 0.f;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) d = fmaf(qf[h][i], kf[i], d);
-                d = row16_sum(d);
-                if (c == 0 && kk < n) sc[h][kk] = d;
-            }
-        }
-    }
-    __syncthreads();
+    };
 
-    // Phase 2: exact max and sum of exp2 over the split, per head.
-    float mx[G], sm[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        float m = -INFINITY;
-        for (int i = tid; i < n; i += 256) m = fmaxf(m, sc[h][i]);
-        m = wave_max(m);
-        if (lane == 0) stat[w][h] = m;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-        mx[h] = fmaxf(fmaxf(stat[0][h], stat[1][h]), fmaxf(stat[2][h], stat[3][h]));
-    __syncthreads();
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        float l = 0.f;
-        for (int i = tid; i < n; i += 256) {
-            const float p = fast_exp2(sc[h][i] - mx[h]);
-            sc[h][i] = p;
-            l += p;
-        }
-        l = wave_sum(l);
-        if (lane == 0) stat[w][h] = l;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int h = 0; h < G; ++h) sm[h] = (stat[0][h] + stat[1][h]) + (stat[2][h] + stat[3][h]);
-
-    // Phase 3: weighted values.
     float acc[G][8];
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[h][i] = 0.f;
-    for (int base = 0; base < n; base += 16 * kUnroll) {
-        u32x4 vv[kUnroll];
+        for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+    // Running max (log2 units) and this lane's share of the sum, per head.
+    float m_run[G], l_run[G];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int kk = base + 16 * u + 4 * w + sub;
-            if (kk < n) {
-                const int64_t row = key_row(table, k0 + kk, a.block_size, a.bs_shift);
-                vv[u] = __builtin_nontemporal_load(
-                    reinterpret_cast<const u32x4 *>(vbase + row * row_stride));
-            } else {
-                vv[u] = u32x4{0, 0, 0, 0};
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int kk = base + 16 * u + 4 * w + sub;
-            if (kk < n) {
-                float vf[8];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    vf[2 * i] = bf16lo(vv[u][i]);
-                    vf[2 * i + 1] = bf16hi(vv[u][i]);
-                }
-#pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    const float p = sc[h][kk];
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) acc[h][i] = fmaf(p, vf[i], acc[h][i]);
-                }
-            }
-        }
+    for (int h = 0; h < G; ++h) {
+        m_run[h] = -INFINITY;
+        l_run[h] = 0.f;
     }
-    // Sum over the wave's 4 key slots (lanes c, c+16, c+32, c+48 hold the same dims).
+
+    // One chunk: raw scores q.k, online softmax (max kept in raw units, probabilities as
+    // exp2(scale * log2(e) * (s - max))), then P.V into the accumulators.
+    auto process = [&](const Chunk &buf, int ch) {
+        const int kc = ch * kChunk;
+        const bool full = kc + kChunk <= n;  // wave-uniform: only the tail chunk masks
+        float sv[kRowLoads][G];
+#pragma unroll
+        for (int i = 0; i < kRowLoads; ++i) {
+            const bool ok = full || kc + 4 * i + sub < n;
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                float d = 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t kw = buf.k[i][e];
+                    d = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(kw), as_bf16x2(qp[h][e]), d,
+                                                        false);
+                }
+                d = row16_sum(d);
+                sv[i][h] = ok ? d : -INFINITY;
+            }
+        }
+        float alpha[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float cm = sv[0][h];
+#pragma unroll
+            for (int i = 1; i < kRowLoads; ++i) cm = fmaxf(cm, sv[i][h]);
+            cm = fmaxf(cm, __shfl_xor(cm, 16));
+            cm = fmaxf(cm, __shfl_xor(cm, 32));
+            const float m_new = fmaxf(m_run[h], cm);
+            alpha[h] = fast_exp2((m_run[h] - m_new) * a.scale_log2);  // 0 on the first chunk
+            m_run[h] = m_new;
+            const float msc = m_new * a.scale_log2;
+            float ps = 0.f;
+#pragma unroll
+            for (int i = 0; i < kRowLoads; ++i) {
+                sv[i][h] = fast_exp2(fmaf(sv[i][h], a.scale_log2, -msc));
+                ps += sv[i][h];
+            }
+            l_run[h] = l_run[h] * alpha[h] + ps;
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[h][e] *= alpha[h];
+#pragma unroll
+        for (int i = 0; i < kRowLoads; ++i) {
+            float vf[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                vf[2 * e] = bf16lo(buf.v[i][e]);
+                vf[2 * e + 1] = bf16hi(buf.v[i][e]);
+            }
+#pragma unroll
+            for (int h = 0; h < G; ++h)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(sv[i][h], vf[e], acc[h][e]);
+        }
+    };
+
+    // Two register buffers: the next chunk is in flight while the current one is processed.
+    const int nch = (n + kChunk - 1) / kChunk;
+    Chunk A, B;
+    int ch = w;
+    if (ch < nch) load_chunk(A, ch);
+    while (ch < nch) {
+        if (ch + 4 < nch) load_chunk(B, ch + 4);
+        process(A, ch);
+        ch += 4;
+        if (ch >= nch) break;
+        if (ch + 4 < nch) load_chunk(A, ch + 4);
+        process(B, ch);
+        ch += 4;
+    }
+
+    // Merge: within the wave (sum over the 4 key slots), then across the 4 waves.
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            float x = acc[h][i];
+        for (int e = 0; e < 8; ++e) {
+            float x = acc[h][e];
             x += __shfl_xor(x, 16);
             x += __shfl_xor(x, 32);
-            acc[h][i] = x;
+            acc[h][e] = x;
         }
     if (sub == 0) {
 #pragma unroll
         for (int h = 0; h < G; ++h)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) red[w][h][8 * c + i] = acc[h][i];
+            for (int e = 0; e < 8; ++e) sm.o[w][h][8 * dc + e] = acc[h][e];
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        float l = l_run[h];
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        if (lane == 0) {
+            sm.ml[w][h][0] = m_run[h] * a.scale_log2;  // -inf for a wave without keys
+            sm.ml[w][h][1] = l;
+        }
     }
     __syncthreads();
 
     for (int idx = tid; idx < G * kHeadDim; idx += 256) {
         const int h = idx / kHeadDim, e = idx % kHeadDim;
-        const float o = (red[0][h][e] + red[1][h][e]) + (red[2][h][e] + red[3][h][e]);
+        float M = sm.ml[0][h][0];
+#pragma unroll
+        for (int ww = 1; ww < 4; ++ww) M = fmaxf(M, sm.ml[ww][h][0]);
+        float num = 0.f, den = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) {
+            const float f = fast_exp2(sm.ml[ww][h][0] - M);  // 0 for a wave without keys
+            num = fmaf(f, sm.o[ww][h][e], num);
+            den = fmaf(f, sm.ml[ww][h][1], den);
+        }
         const int64_t bh = (int64_t)b * a.num_heads + g * G + h;
         if (nsplit == 1) {
-            const float r = o / sm[h];
-            a.out[bh * kHeadDim + e] = __builtin_bit_cast(uint16_t, (__bf16)r);
+            a.out[bh * kHeadDim + e] = __builtin_bit_cast(uint16_t, (__bf16)(num / den));
         } else {
-            a.ws_o[(bh * a.max_splits + s) * kHeadDim + e] = o;
+            a.ws_o[(bh * a.max_splits + s) * kHeadDim + e] = num;
             if (e == 0) {
-                a.ws_ml[(bh * a.max_splits + s) * 2] = mx[h];
-                a.ws_ml[(bh * a.max_splits + s) * 2 + 1] = sm[h];
+                a.ws_ml[(bh * a.max_splits + s) * 2] = M;
+                a.ws_ml[(bh * a.max_splits + s) * 2 + 1] = den;
             }
         }
     }
@@ -230,7 +305,7 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
         return;
     }
     const int nsplit = (L + a.split_keys - 1) / a.split_keys;
-    if (nsplit == 1) return;  // the partial kernel wrote the final row
+    if (nsplit == 1) return;  // the split kernel wrote the final row
     const float *ml = a.ws_ml + bh * a.max_splits * 2;
     float M = -INFINITY;
     for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ml[2 * s]);
@@ -245,8 +320,8 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
 
 template <int G>
 nv_status launch_decode(const DecodeArgs &a, int batch, hipStream_t stream) {
-    nv_status st = launch(decode_partial_kernel<G>,
-                          dim3(a.max_splits, a.num_kv_heads, batch), dim3(256), 0, stream, a);
+    nv_status st = launch(decode_split_kernel<G>, dim3(a.max_splits, a.num_kv_heads, batch),
+                          dim3(256), 0, stream, a);
     if (st != NV_OK) return st;
     return launch(decode_combine_kernel, dim3(a.num_heads, batch), dim3(kHeadDim), 0, stream, a);
 }
@@ -262,12 +337,13 @@ extern "C" int32_t nv_paged_attn_decode_split_keys(int32_t batch, int32_t num_kv
                                                    int32_t max_blocks_per_seq,
                                                    int32_t block_size) {
     using namespace nvp;
-    // Largest split (fewest partials) that still yields >= 2048 work items over the padded
-    // context, so small batches spread over all 256 CUs.
+    // Largest split (fewest partials) that still yields enough work items over the padded
+    // context, so every CU gets work; capped so that one split's table slice fits in LDS.
     const int64_t ctx = max_context(max_blocks_per_seq, block_size);
+    const int64_t cap = (int64_t)(kTableSlots - 2) * (block_size > 0 ? block_size : 1);
     int32_t S = kMaxSplitKeys;
     while (S > kMinSplitKeys &&
-           (int64_t)batch * num_kv_heads * ((ctx + S - 1) / S) < 2048)
+           (S > cap || (int64_t)batch * num_kv_heads * ((ctx + S - 1) / S) < NV_DECODE_TARGET_ITEMS))
         S /= 2;
     return S;
 }
@@ -303,11 +379,13 @@ extern "C" nv_status nv_paged_attn_decode(const void *q, const void *k_cache,
         max_blocks_per_seq < 0)
         return NV_ERR_INVALID_ARG;
     if (num_heads % num_kv_heads != 0) return NV_ERR_INVALID_ARG;
+    if (!(softmax_scale > 0.f) || softmax_scale == INFINITY) return NV_ERR_INVALID_ARG;
     if (head_dim != kHeadDim) return NV_ERR_UNSUPPORTED;
     const int G = num_heads / num_kv_heads;
     if (G > 8) return NV_ERR_UNSUPPORTED;
     if (batch == 0) return NV_OK;
     if (!q || !k_cache || !v_cache || !context_lens || !out) return NV_ERR_INVALID_ARG;
+    if (batch > 65535 || num_kv_heads > 65535) return NV_ERR_UNSUPPORTED;
     if (max_blocks_per_seq == 0) {
         // No sequence can hold a key: every row is a padding row; only the zeros are written.
         DecodeArgs z{};
@@ -316,7 +394,6 @@ extern "C" nv_status nv_paged_attn_decode(const void *q, const void *k_cache,
         z.num_heads = num_heads;
         z.split_keys = kMaxSplitKeys;
         z.max_splits = 1;
-        if (batch > 65535) return NV_ERR_UNSUPPORTED;
         return launch(decode_combine_kernel, dim3(num_heads, batch), dim3(kHeadDim), 0, stream, z);
     }
     if (!block_tables) return NV_ERR_INVALID_ARG;
@@ -342,7 +419,7 @@ extern "C" nv_status nv_paged_attn_decode(const void *q, const void *k_cache,
                                                    block_size);
     const int64_t splits = (max_context(max_blocks_per_seq, block_size) + a.split_keys - 1) /
                            a.split_keys;
-    if (splits > 65535 || batch > 65535 || num_kv_heads > 65535) return NV_ERR_UNSUPPORTED;
+    if (splits > 65535) return NV_ERR_UNSUPPORTED;
     a.max_splits = (int32_t)splits;
     const size_t rows = (size_t)batch * num_heads * splits;
     const size_t ml_bytes = (rows * 2 * sizeof(float) + 255) / 256 * 256;

@@ -34,6 +34,13 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// A packed bf16 pair as the operand type of the bf16 dot builtins. Takes the word by value:
+// applying __builtin_bit_cast directly to a vector-element expression (x[e]) is miscompiled by
+// this compiler (every element reads as element 0), a scalar copy is not.
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t word) {
+    return __builtin_bit_cast(bf16x2, word);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Sum over each row of 16 lanes via DPP rotations; every lane of the row gets the total.

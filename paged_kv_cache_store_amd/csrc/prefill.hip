@@ -269,6 +269,7 @@ extern "C" nv_status nv_paged_attn_prefill(const void *q, const void *k_cache,
         max_seqlen_q < 0 || max_seqlen_k < 0 || max_blocks_per_seq < 0)
         return NV_ERR_INVALID_ARG;
     if (num_heads % num_kv_heads != 0) return NV_ERR_INVALID_ARG;
+    if (!(softmax_scale > 0.f) || softmax_scale == INFINITY) return NV_ERR_INVALID_ARG;
     if (max_seqlen_q > max_seqlen_k) return NV_ERR_INVALID_ARG;
     if ((int64_t)max_seqlen_k > (int64_t)max_blocks_per_seq * block_size)
         return NV_ERR_INVALID_ARG;

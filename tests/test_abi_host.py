@@ -153,12 +153,18 @@ def test_device_calls_reject_bad_arguments_without_launch(nv):
 
 
 def test_decode_split_choice(nv):
-    # Small batches get short splits so the chip fills; large ones get 512-key splits.
-    assert nv.nv_paged_attn_decode_split_keys(6, 8, 3, 256) == 64
-    assert nv.nv_paged_attn_decode_split_keys(256, 8, 16, 256) == 512
-    assert nv.nv_paged_attn_decode_split_keys(512, 8, 16, 256) == 512
-    for b in (1, 3, 17, 100, 600):
+    # Small batches get short splits so the chip fills; large ones get long splits (few
+    # partial results).
+    assert nv.nv_paged_attn_decode_split_keys(6, 8, 3, 256) == 128
+    assert nv.nv_paged_attn_decode_split_keys(256, 8, 16, 256) == 2048
+    assert nv.nv_paged_attn_decode_split_keys(512, 8, 16, 256) == 2048
+    prev = None
+    for b in (1, 3, 17, 100, 600, 5000):
         s = nv.nv_paged_attn_decode_split_keys(b, 8, 16, 256)
-        assert s % 64 == 0 and 64 <= s <= 512
+        assert s % 64 == 0 and 128 <= s <= 2048
+        assert prev is None or s >= prev  # never shorter for a larger batch
+        prev = s
+    # Tiny blocks cap the split so one split's table slice fits the kernel's staging area.
+    assert nv.nv_paged_attn_decode_split_keys(4, 8, 4096, 1) <= 262
     # One split covers every context: no workspace needed.
     assert nv.nv_paged_attn_decode_workspace_size(4096, 16, 8, 128, 1, 256) == 0

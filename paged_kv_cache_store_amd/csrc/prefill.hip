@@ -10,29 +10,49 @@
 //  - A workgroup of 4 waves owns one kv head g, HPW query heads of its group and a tile of
 //    M = 128 / HPW new rows; each wave owns 32 rows of one head. Every K/V tile staged in LDS
 //    is therefore shared by all query heads the workgroup holds.
-//  - K/V are walked in tiles of 64 keys. Each thread looks up its own key's block in the table,
-//    so any block size works and padding entries are never read.
+//  - K/V are walked in tiles of 64 keys, copied from HBM straight into LDS with
+//    global_load_lds (16 bytes per lane, no staging registers) into two LDS stages: the next
+//    tile streams in while the current one is multiplied; one barrier per tile. Each thread
+//    looks up its own key's block in the table, so any block size works and padding entries
+//    are never read (keys past the tile's end re-read the last valid key, then get masked).
+//  - LDS rows are 256 bytes, unpadded; bank conflicts are avoided by XOR-swizzling the 16-byte
+//    chunks of a row (K: chunk ^ (row % 16); V: chunk ^ 2 (row % 4)), applied on the global
+//    side since the copy places lane i's 16 bytes at 16 i.
 //  - Scores are computed transposed, S^T[key, row] = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //    K (A operand) is read from LDS, Q^T (B operand) stays in registers for the whole loop. In
-//    the 32x32 accumulator a lane holds one query row and 16 of its keys, so the softmax
-//    row max is an in-register max plus one swap with the lane 32 away, and the row sum is
-//    kept per lane and merged once at the end.
+//    the 32x32 accumulator a lane holds one query row and 16 of its keys, so the softmax row
+//    max is an in-register max plus one swap with the lane 32 away, and the row sum is kept
+//    per lane and merged once at the end.
 //  - O^T[dim, row] += V^T P^T. The probabilities never leave registers: the accumulator of S^T
-//    already is the B operand layout once converted to bf16; the key order inside each
-//    16-key MFMA step is chosen to match it, and V is written to LDS transposed
-//    (key pairs packed per dim) so each lane reads its 8 keys of one dim with two 8-byte loads.
-//  - Softmax runs in log2 units (scale * log2(e) folded in; exp2 is the hardware exp).
+//    already is the B operand layout once converted to bf16, with the key order inside each
+//    16-key MFMA step chosen to match it. The V^T operand is read from row-major V in LDS
+//    with ds_read_b64_tr_b16 (each 16-lane group turns 4 keys x 16 dims into one dim x 4
+//    keys per lane), two reads per MFMA.
+//  - Softmax in log2 units with the scale folded into one FMA before exp2; masking only on
+//    tiles the causal diagonal or the key end cuts; the output rescale is skipped when no row
+//    max moved.
 //  - Work items are ordered (sequence, kv head, head subgroup, q tile from last to first) and
 //    remapped so consecutive items land on the same XCD: workgroups that read the same K/V
 //    share that XCD's L2.
 #include "nv_common.h"
 
+#ifndef NV_PREFILL_WAVES
+#define NV_PREFILL_WAVES 2  // register budget for this many waves per SIMD
+#endif
+
 namespace nvp {
 namespace {
 
 constexpr int kTileKeys = 64;
-constexpr int kKPitch = kHeadDim + 8;     // bf16 per K row in LDS (272 B: conflict-free reads)
-constexpr int kVPitch = kTileKeys + 4;    // bf16 per transposed V row in LDS (136 B)
+constexpr int kRowBytes = kHeadDim * 2;           // one key row of one kv head in LDS
+constexpr int kTileBytes = kTileKeys * kRowBytes;  // 16 KiB
+
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4v;
+#define NV_LDS __attribute__((address_space(3)))
+
+// 16-byte chunk position of logical chunk c of tile row r in LDS.
+__device__ __forceinline__ int k_chunk_pos(int r, int c) { return c ^ (r & 15); }
+__device__ __forceinline__ int v_chunk_pos(int r, int c) { return c ^ ((r & 3) << 1); }
 
 struct PrefillArgs {
     const uint16_t *q;
@@ -55,11 +75,11 @@ struct PrefillArgs {
 };
 
 template <int HPW>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NV_PREFILL_WAVES))) void prefill_kernel(PrefillArgs a) {
     constexpr int kWavesPerHead = 4 / HPW;
     constexpr int M = 32 * kWavesPerHead;  // rows per workgroup
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[kTileKeys * kKPitch];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[kHeadDim * kVPitch];
+    // Two stages of K and V tiles (row-major, swizzled): 64 KiB.
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2][kTileBytes];
 
     // XCD-aware remap: hardware hands consecutive workgroup ids to different XCDs; give each
     // XCD a contiguous range of work items.
@@ -104,59 +124,45 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
         }
     }
 
+    // ---- HBM -> LDS copy of the tile at key0 into stage st ----
+    // Wave w, instruction j moves tile rows 16w + 4j .. +3 (1 KiB, contiguous in LDS); lane i
+    // lands at 16 i: row 16w + 4j + i/16, chunk position i%16, i.e. logical chunk
+    // position ^ swizzle(row) of that row.
+    auto copy_tile = [&](int key0, int st) {
+        const int pos = lane & 15;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 16 * w + 4 * j + (lane >> 4);
+            const int key = min(key0 + r, kv_end - 1);  // past the end: a valid row, masked later
+            const int64_t row = key_row(table, key, a.block_size, a.bs_shift);
+            const uint16_t *kg = a.k_cache + row * kv_row_stride + g * kHeadDim;
+            const uint16_t *vg = a.v_cache + row * kv_row_stride + g * kHeadDim;
+            NV_LDS void *kd = (NV_LDS void *)&lds[st][0][(16 * w + 4 * j) * kRowBytes];
+            NV_LDS void *vd = (NV_LDS void *)&lds[st][1][(16 * w + 4 * j) * kRowBytes];
+            __builtin_amdgcn_global_load_lds(kg + 8 * (pos ^ (r & 15)), kd, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vg + 8 * (pos ^ ((r & 3) << 1)), vd, 16, 0, 0);
+        }
+    };
+
     f32x16 o[4];
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[d][i] = 0.f;
-    float m_run = -INFINITY;  // running max (log2 units) of this lane's row
+    float m_run = -INFINITY;  // running max of this lane's row, raw score units
     float l_part = 0.f;       // this lane's share of the row sum
 
+    copy_tile(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    const int vt = lane & 15, vj = lane >> 4;  // lane in its 16-lane group, group index
     for (int t = 0; t < n_tiles; ++t) {
+        const int st = t & 1;
         const int key0 = t * kTileKeys;
-        // ---- stage K (row-major) and V (transposed) of keys [key0, key0 + 64) in LDS ----
-        {
-            const int chunk = tid & 15;
-#pragma unroll
-            for (int pass = 0; pass < 4; ++pass) {
-                const int kk = pass * 16 + (tid >> 4);
-                const int j = key0 + kk;
-                u32x4 v = u32x4{0, 0, 0, 0};
-                if (j < kv_end) {
-                    const int64_t row = key_row(table, j, a.block_size, a.bs_shift);
-                    v = *reinterpret_cast<const u32x4 *>(a.k_cache + row * kv_row_stride +
-                                                         g * kHeadDim + 8 * chunk);
-                }
-                *reinterpret_cast<u32x4 *>(&Ks[kk * kKPitch + 8 * chunk]) = v;
-            }
-            const int pr = tid & 31, dg = tid >> 5;  // key pair, 16-dim group
-            u32x4 va[2], vb[2];
-            {
-                const int j = key0 + 2 * pr;
-                va[0] = va[1] = vb[0] = vb[1] = u32x4{0, 0, 0, 0};
-                if (j < kv_end) {
-                    const int64_t row = key_row(table, j, a.block_size, a.bs_shift);
-                    const uint16_t *p = a.v_cache + row * kv_row_stride + g * kHeadDim + 16 * dg;
-                    va[0] = *reinterpret_cast<const u32x4 *>(p);
-                    va[1] = *reinterpret_cast<const u32x4 *>(p + 8);
-                }
-                if (j + 1 < kv_end) {
-                    const int64_t row = key_row(table, j + 1, a.block_size, a.bs_shift);
-                    const uint16_t *p = a.v_cache + row * kv_row_stride + g * kHeadDim + 16 * dg;
-                    vb[0] = *reinterpret_cast<const u32x4 *>(p);
-                    vb[1] = *reinterpret_cast<const u32x4 *>(p + 8);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const uint32_t x = va[i >> 3][(i >> 1) & 3];
-                const uint32_t y = vb[i >> 3][(i >> 1) & 3];
-                const uint32_t packed = (i & 1) ? ((x >> 16) | (y & 0xffff0000u))
-                                                : ((x & 0xffffu) | (y << 16));
-                *reinterpret_cast<uint32_t *>(&Vt[(16 * dg + i) * kVPitch + 2 * pr]) = packed;
-            }
-        }
-        __syncthreads();
+        if (t + 1 < n_tiles) copy_tile(key0 + kTileKeys, st ^ 1);  // streams in meanwhile
+        const uint8_t *Ks = lds[st][0];
+        const uint8_t *Vs = lds[st][1];
 
         // ---- S^T = K Q^T for two 32-key blocks ----
         f32x16 s[2];
@@ -164,46 +170,60 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-            const uint16_t *kp = &Ks[(kb * 32 + col) * kKPitch + 8 * hg];
+            const int r = kb * 32 + col;
 #pragma unroll
-            for (int st = 0; st < 8; ++st) {
-                const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kp + 16 * st);
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[st], s[kb], 0, 0, 0);
+            for (int kt = 0; kt < 8; ++kt) {
+                const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(
+                    Ks + r * kRowBytes + 16 * k_chunk_pos(r, 2 * kt + hg));
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[kt], s[kb], 0, 0, 0);
             }
         }
 
-        // ---- mask, online softmax (log2 units) ----
-        const int vis_end = min(Lk, P + my_row + 1);  // keys [0, vis_end) visible to my row
-        float tmax = -INFINITY;
+        // ---- mask (only tiles the diagonal or the key end cuts), online softmax ----
+        // Row i of the wave sees keys < P + r0 + i + 1; the whole tile is visible to every
+        // row of the wave when its last key is <= P + r0 (and below Lk).
+        if (key0 + kTileKeys - 1 > P + r0 || key0 + kTileKeys > Lk) {
+            const int vis_end = min(Lk, P + my_row + 1);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int j = key0 + kb * 32 + 8 * (i >> 2) + 4 * hg + (i & 3);
+                    if (j >= vis_end) s[kb][i] = -INFINITY;
+                }
+        }
+        float tmax = s[0][0];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int j = key0 + kb * 32 + 8 * (i >> 2) + 4 * hg + (i & 3);
-                const float x = j < vis_end ? s[kb][i] * a.scale_log2 : -INFINITY;
-                s[kb][i] = x;
-                tmax = fmaxf(tmax, x);
-            }
+            for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[kb][i]);
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float m_new = fmaxf(m_run, tmax);
-        const float alpha = fast_exp2(m_run - m_new);  // 0 on the first tile
-        m_run = m_new;
+        const float m_new = fmaxf(m_run, tmax);  // finite: key 0 is visible to every row
+        if (__any(m_new != m_run)) {  // rescale only when some row's max moved
+            const float alpha = fast_exp2((m_run - m_new) * a.scale_log2);  // 0 on the first tile
+            l_part *= alpha;
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) o[d][i] *= alpha;
+            m_run = m_new;
+        }
+        const float msc = m_run * a.scale_log2;
         float psum = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const float p = fast_exp2(s[kb][i] - m_new);
+                const float p = fast_exp2(fmaf(s[kb][i], a.scale_log2, -msc));
                 s[kb][i] = p;
                 psum += p;
             }
-        l_part = l_part * alpha + psum;
-#pragma unroll
-        for (int d = 0; d < 4; ++d)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) o[d][i] *= alpha;
+        l_part += psum;
 
         // ---- O^T += V^T P^T, 16 keys per MFMA step ----
+        // V^T operand of lane (group vj, lane vt): dim 32 d + 16 (vj & 1) + vt, keys
+        // 16u + 4hg + {0..3} (first read) and 16u + 8 + 4hg + {0..3} (second read); the read
+        // address of lane vt is row 16u + 4hg + vt/4 (+8), dims 16 (vj & 1) + 4 (vt%4) .. +3.
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int kb = u >> 1, ib = 8 * (u & 1);
@@ -211,16 +231,20 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) pw[e] = pack_bf16(s[kb][ib + 2 * e], s[kb][ib + 2 * e + 1]);
             const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+            const int ra = 16 * u + 4 * hg + (vt >> 2), rb = ra + 8;
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
-                const uint16_t *vp = &Vt[(32 * d + col) * kVPitch + 16 * u + 4 * hg];
-                const u32x2 lo = *reinterpret_cast<const u32x2 *>(vp);
-                const u32x2 hi = *reinterpret_cast<const u32x2 *>(vp + 8);
-                const u32x4 vw = u32x4{lo[0], lo[1], hi[0], hi[1]};
-                o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vw),
-                                                              pb, o[d], 0, 0, 0);
+                const int dim = 32 * d + 16 * (vj & 1) + 4 * (vt & 3);
+                const int ca = v_chunk_pos(ra, dim >> 3), cb = v_chunk_pos(rb, dim >> 3);
+                const bf16x4v va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (NV_LDS bf16x4v *)(Vs + ra * kRowBytes + 16 * ca + 2 * (dim & 7)));
+                const bf16x4v vb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (NV_LDS bf16x4v *)(Vs + rb * kRowBytes + 16 * cb + 2 * (dim & 7)));
+                const bf16x8 vw = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
+                o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vw, pb, o[d], 0, 0, 0);
             }
         }
+        __builtin_amdgcn_s_waitcnt(0);  // this thread's copies of the next tile have landed
         __syncthreads();
     }
 

@@ -102,7 +102,7 @@ nv_status nv_store_kvcache(const void *key, int64_t key_row_stride,
  *   softmax_scale  positive and finite; the engine passes head_dim ** -0.5.
  *   out            device bf16 [total_q, num_heads, head_dim] contiguous; may not alias q.
  * Supported: head_dim == 128, num_heads % num_kv_heads == 0, (num_heads / num_kv_heads) <= 8,
- * block_size >= 1. block_tables == NULL (the packed fresh-K/V mode of the engine's first
+ * block_size >= 1, ceil(max_seqlen_k / block_size) <= 2048. block_tables == NULL (the packed fresh-K/V mode of the engine's first
  * prefill) returns NV_ERR_UNSUPPORTED: store first, then attend through the table.
  * ------------------------------------------------------------------------------------------ */
 nv_status nv_paged_attn_prefill(const void *q, const void *k_cache, const void *v_cache,

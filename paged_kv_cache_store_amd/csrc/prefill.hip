@@ -7,9 +7,10 @@
 // head; query head h reads kv head h / G.
 //
 // gfx950 design (bf16 MFMA, fp32 accumulation, online softmax):
-//  - A workgroup of 4 waves owns one kv head g, HPW query heads of its group and a tile of
-//    M = 128 / HPW new rows; each wave owns 32 rows of one head. Every K/V tile staged in LDS
-//    is therefore shared by all query heads the workgroup holds.
+//  - A workgroup of W waves (4, or 8 when the context is long next to the new tokens) owns one
+//    kv head g, HPW query heads of its group and a tile of M = 32 W / HPW new rows; each wave
+//    owns 32 rows of one head. Every K/V tile staged in LDS is therefore shared by all query
+//    heads and rows the workgroup holds.
 //  - K/V are walked in tiles of 64 keys, copied from HBM straight into LDS with
 //    global_load_lds (16 bytes per lane, no staging registers) into two LDS stages: the next
 //    tile streams in while the current one is multiplied; one barrier per tile. Each thread
@@ -36,19 +37,61 @@
 //    share that XCD's L2.
 #include "nv_common.h"
 
+#include <type_traits>
+
 #ifndef NV_PREFILL_WAVES
 #define NV_PREFILL_WAVES 2  // register budget for this many waves per SIMD
+#endif
+#ifndef NV_PREFILL_SETPRIO
+#define NV_PREFILL_SETPRIO 0  // raise the wave priority while it issues MFMA groups
+#endif
+#ifndef NV_PREFILL_STAGES
+#define NV_PREFILL_STAGES 2    // LDS stages of K/V tiles (2 or 3)
+#endif
+
+#if NV_PREFILL_SETPRIO
+#define NV_PRIO_HI() __builtin_amdgcn_s_setprio(1)
+#define NV_PRIO_LO() __builtin_amdgcn_s_setprio(0)
+#else
+#define NV_PRIO_HI()
+#define NV_PRIO_LO()
 #endif
 
 namespace nvp {
 namespace {
 
 constexpr int kTileKeys = 64;
+constexpr int kTableSlots = 2048;  // block-table entries staged in LDS (caps max_seqlen_k / block_size)
 constexpr int kRowBytes = kHeadDim * 2;           // one key row of one kv head in LDS
 constexpr int kTileBytes = kTileKeys * kRowBytes;  // 16 KiB
 
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4v;
 #define NV_LDS __attribute__((address_space(3)))
+
+// Asynchronous copy of 16 bytes per lane from global memory into LDS: lane i's bytes land at
+// lds_base + 16 i (lds_base wave-uniform). Issued through inline assembly so that the
+// compiler's wait insertion does not treat the in-flight copy as aliasing every LDS read
+// (it would drain the copy before each one); completion is waited for explicitly
+// (s_waitcnt vmcnt) before the barrier that publishes a tile.
+__device__ __forceinline__ void copy16_to_lds(const void *src, void *lds_base) {
+    const uint32_t base = (uint32_t)(uintptr_t)lds_base;
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(base)), "v"(src)
+                 : "memory", "m0");
+}
+
+// Waits until at most N of this wave's memory loads are outstanding and all its LDS accesses
+// are done (loads complete in order, so the older tile's copies have landed), then meets the
+// workgroup at a barrier. Unlike __syncthreads this does not drain the younger copies.
+template <int N>
+__device__ __forceinline__ void wait_copies_and_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4));  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 // 16-byte chunk position of logical chunk c of tile row r in LDS.
 __device__ __forceinline__ int k_chunk_pos(int r, int c) { return c ^ (r & 15); }
@@ -74,12 +117,16 @@ struct PrefillArgs {
     float scale_log2;
 };
 
-template <int HPW>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NV_PREFILL_WAVES))) void prefill_kernel(PrefillArgs a) {
-    constexpr int kWavesPerHead = 4 / HPW;
+template <int HPW, int kWaves>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(NV_PREFILL_WAVES))) void prefill_kernel(PrefillArgs a) {
+    constexpr int kWavesPerHead = kWaves / HPW;
     constexpr int M = 32 * kWavesPerHead;  // rows per workgroup
-    // Two stages of K and V tiles (row-major, swizzled): 64 KiB.
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2][kTileBytes];
+    // NS stages of K and V tiles (row-major, swizzled), 32 KiB per stage; the stage index is
+    // always a compile-time constant.
+    constexpr int NS = NV_PREFILL_STAGES;
+    __shared__ __attribute__((aligned(1024))) uint8_t k_lds[NS][kTileBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t v_lds[NS][kTileBytes];
+    __shared__ int32_t tbl[kTableSlots];  // the sequence's first block ids, staged once
 
     // XCD-aware remap: hardware hands consecutive workgroup ids to different XCDs; give each
     // XCD a contiguous range of work items.
@@ -124,23 +171,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NV_PREFILL_
         }
     }
 
+    // Block ids of the keys this workgroup reads, staged in LDS so that no copy address waits
+    // on a global load (the host guarantees they fit: ceil(max_seqlen_k / block_size) <=
+    // kTableSlots).
+    const int n_blocks = a.bs_shift >= 0 ? (kv_end + a.block_size - 1) >> a.bs_shift
+                                         : (kv_end + a.block_size - 1) / a.block_size;
+    for (int i = tid; i < n_blocks; i += kWaves * 64) tbl[i] = table[i];
+    auto key_row_staged = [&](int j) -> int64_t {
+        int lb, off;
+        if (a.bs_shift >= 0) {
+            lb = j >> a.bs_shift;
+            off = j & (a.block_size - 1);
+        } else {
+            lb = j / a.block_size;
+            off = j - lb * a.block_size;
+        }
+        return (int64_t)tbl[lb] * a.block_size + off;
+    };
+    __syncthreads();
+
     // ---- HBM -> LDS copy of the tile at key0 into stage st ----
     // Wave w, instruction j moves tile rows 16w + 4j .. +3 (1 KiB, contiguous in LDS); lane i
     // lands at 16 i: row 16w + 4j + i/16, chunk position i%16, i.e. logical chunk
     // position ^ swizzle(row) of that row.
-    auto copy_tile = [&](int key0, int st) {
+    auto copy_tile = [&](int key0, auto stage) {
+        constexpr int st = decltype(stage)::value;
+        uint8_t *kl = k_lds[st];
+        uint8_t *vl = v_lds[st];
         const int pos = lane & 15;
+        constexpr int kRowsPerWave = kTileKeys / kWaves;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 16 * w + 4 * j + (lane >> 4);
+        for (int j = 0; j < kRowsPerWave / 4; ++j) {
+            const int r = kRowsPerWave * w + 4 * j + (lane >> 4);
             const int key = min(key0 + r, kv_end - 1);  // past the end: a valid row, masked later
-            const int64_t row = key_row(table, key, a.block_size, a.bs_shift);
+            const int64_t row = key_row_staged(key);
             const uint16_t *kg = a.k_cache + row * kv_row_stride + g * kHeadDim;
             const uint16_t *vg = a.v_cache + row * kv_row_stride + g * kHeadDim;
-            NV_LDS void *kd = (NV_LDS void *)&lds[st][0][(16 * w + 4 * j) * kRowBytes];
-            NV_LDS void *vd = (NV_LDS void *)&lds[st][1][(16 * w + 4 * j) * kRowBytes];
-            __builtin_amdgcn_global_load_lds(kg + 8 * (pos ^ (r & 15)), kd, 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(vg + 8 * (pos ^ ((r & 3) << 1)), vd, 16, 0, 0);
+            copy16_to_lds(kg + 8 * k_chunk_pos(r, pos), &kl[(kRowsPerWave * w + 4 * j) * kRowBytes]);
+            copy16_to_lds(vg + 8 * v_chunk_pos(r, pos), &vl[(kRowsPerWave * w + 4 * j) * kRowBytes]);
         }
     };
 
@@ -152,19 +220,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NV_PREFILL_
     float m_run = -INFINITY;  // running max of this lane's row, raw score units
     float l_part = 0.f;       // this lane's share of the row sum
 
-    copy_tile(0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    // Copies in flight per thread per tile (loads complete in order).
+    constexpr int kCopiesPerTile = 2 * (kTileKeys / kWaves) / 4;
+    // Prologue: tiles 0 .. NS-2 start streaming in.
+    copy_tile(0, std::integral_constant<int, 0>{});
+    if constexpr (NS > 2) {
+        if (1 < n_tiles) copy_tile(kTileKeys, std::integral_constant<int, 1>{});
+    }
 
     const int vt = lane & 15, vj = lane >> 4;  // lane in its 16-lane group, group index
-    for (int t = 0; t < n_tiles; ++t) {
-        const int st = t & 1;
+    // One tile: wait for its copies, publish it with a barrier (which also retires the stage
+    // of tile t-1), start copying tile t + NS - 1 into that stage, multiply tile t.
+    auto tile_step = [&](int t, auto stage) {
+        constexpr int st = decltype(stage)::value;
         const int key0 = t * kTileKeys;
-        if (t + 1 < n_tiles) copy_tile(key0 + kTileKeys, st ^ 1);  // streams in meanwhile
-        const uint8_t *Ks = lds[st][0];
-        const uint8_t *Vs = lds[st][1];
+        if (NS > 2 && t + 1 < n_tiles) wait_copies_and_barrier<kCopiesPerTile>();
+        else wait_copies_and_barrier<0>();
+        if (t + NS - 1 < n_tiles)
+            copy_tile(key0 + (NS - 1) * kTileKeys,
+                      std::integral_constant<int, (st + NS - 1) % NS>{});
+        const uint8_t *Ks = k_lds[st];
+        const uint8_t *Vs = v_lds[st];
 
         // ---- S^T = K Q^T for two 32-key blocks ----
+        NV_PRIO_HI();
         f32x16 s[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -179,6 +258,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NV_PREFILL_
             }
         }
 
+        NV_PRIO_LO();
         // ---- mask (only tiles the diagonal or the key end cuts), online softmax ----
         // Row i of the wave sees keys < P + r0 + i + 1; the whole tile is visible to every
         // row of the wave when its last key is <= P + r0 (and below Lk).
@@ -221,6 +301,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NV_PREFILL_
         l_part += psum;
 
         // ---- O^T += V^T P^T, 16 keys per MFMA step ----
+        NV_PRIO_HI();
         // V^T operand of lane (group vj, lane vt): dim 32 d + 16 (vj & 1) + vt, keys
         // 16u + 4hg + {0..3} (first read) and 16u + 8 + 4hg + {0..3} (second read); the read
         // address of lane vt is row 16u + 4hg + vt/4 (+8), dims 16 (vj & 1) + 4 (vt%4) .. +3.
@@ -244,8 +325,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NV_PREFILL_
                 o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vw, pb, o[d], 0, 0, 0);
             }
         }
-        __builtin_amdgcn_s_waitcnt(0);  // this thread's copies of the next tile have landed
-        __syncthreads();
+        NV_PRIO_LO();
+    };
+    for (int t = 0; t < n_tiles; t += NS) {
+        tile_step(t, std::integral_constant<int, 0>{});
+        if (t + 1 < n_tiles) tile_step(t + 1, std::integral_constant<int, 1>{});
+        if constexpr (NS > 2) {
+            if (t + 2 < n_tiles) tile_step(t + 2, std::integral_constant<int, 2>{});
+        }
     }
 
     // ---- normalise and store: lane holds row `col`, dims 32d + 8(i/4) + 4hg + (i%4) ----
@@ -265,16 +352,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NV_PREFILL_
     }
 }
 
-template <int HPW>
+template <int HPW, int kWaves>
 nv_status launch_prefill(PrefillArgs a, int batch, int max_seqlen_q, hipStream_t stream) {
-    constexpr int M = 128 / HPW;
+    constexpr int M = 32 * kWaves / HPW;
     a.n_qtiles = (max_seqlen_q + M - 1) / M;
     const int64_t items = (int64_t)batch * a.num_kv_heads * (a.group / HPW) * a.n_qtiles;
     if (items == 0) return NV_OK;
     if (items > (int64_t)INT32_MAX / 2) return NV_ERR_UNSUPPORTED;
     a.items = (int32_t)items;
     a.items_per_xcd = (int32_t)((items + 7) / 8);
-    return launch(prefill_kernel<HPW>, dim3(8 * a.items_per_xcd), dim3(256), 0, stream, a);
+    return launch(prefill_kernel<HPW, kWaves>, dim3(8 * a.items_per_xcd), dim3(64 * kWaves), 0,
+                  stream, a);
+}
+
+// 8-wave workgroups (twice the query rows per K/V tile) pay off when each row sees a long
+// context: chunked or prefix-cached prefill. Fresh prompts keep 4 waves (more workgroups).
+template <int HPW>
+nv_status launch_prefill_sized(PrefillArgs a, int batch, int max_seqlen_q, int max_seqlen_k,
+                               hipStream_t stream) {
+    if (max_seqlen_k >= 2 * max_seqlen_q)
+        return launch_prefill<HPW, 8>(a, batch, max_seqlen_q, stream);
+    return launch_prefill<HPW, 4>(a, batch, max_seqlen_q, stream);
 }
 
 }  // namespace
@@ -300,6 +398,8 @@ extern "C" nv_status nv_paged_attn_prefill(const void *q, const void *k_cache,
     if (head_dim != kHeadDim) return NV_ERR_UNSUPPORTED;
     const int G = num_heads / num_kv_heads;
     if (G > 8) return NV_ERR_UNSUPPORTED;
+    if (((int64_t)max_seqlen_k + block_size - 1) / block_size > kTableSlots)
+        return NV_ERR_UNSUPPORTED;  // the block-table prefix must fit the LDS staging area
     if (batch == 0 || max_seqlen_q == 0) return NV_OK;
     if (!block_tables) return NV_ERR_UNSUPPORTED;  // packed fresh-K/V mode not built
     if (!q || !k_cache || !v_cache || !cu_seqlens_q || !cu_seqlens_k || !out)
@@ -320,6 +420,6 @@ extern "C" nv_status nv_paged_attn_prefill(const void *q, const void *k_cache,
     a.bs_shift = (block_size & (block_size - 1)) == 0 ? __builtin_ctz((unsigned)block_size) : -1;
     a.scale_log2 = softmax_scale * kLog2e;
     a.n_qtiles = a.items = a.items_per_xcd = 0;
-    if (G % 2 == 0) return launch_prefill<2>(a, batch, max_seqlen_q, stream);
-    return launch_prefill<1>(a, batch, max_seqlen_q, stream);
+    if (G % 2 == 0) return launch_prefill_sized<2>(a, batch, max_seqlen_q, max_seqlen_k, stream);
+    return launch_prefill_sized<1>(a, batch, max_seqlen_q, max_seqlen_k, stream);
 }

@@ -137,6 +137,11 @@ def test_device_calls_reject_bad_arguments_without_launch(nv):
                                    null) == -1  # max_seqlen_q > max_seqlen_k
     assert L.nv_paged_attn_prefill(1, 1, 1, 1, 1, 8, 300, 1, 1, 1, 8, 4, 128, 256, 0.1, 1,
                                    null) == -1  # keys beyond the table width
+    assert L.nv_paged_attn_prefill(1, 1, 1, 1, 1, 8, 2049, 1, 3000, 1, 8, 4, 128, 1, 0.1, 1,
+                                   null) == -2  # table prefix larger than the LDS staging area
+    assert L.nv_paged_attn_prefill(*args, 8, 4, 128, 256, -0.1, 1, null) == -1  # scale <= 0
+    assert L.nv_paged_attn_decode(1, 1, 1, 1, 1, 3, 4, 16, 8, 128, 256, 0.0, 256, 1 << 30, 1,
+                                  null) == -1  # scale <= 0
     # decode: workspace too small
     need = nv.nv_paged_attn_decode_workspace_size(4, 16, 8, 128, 3, 256)
     assert need > 0

@@ -127,3 +127,16 @@ def test_config_mixed_8b_sampled():
     w = workloads.config_mixed_8b()
     ids = sorted(np.random.default_rng(1).choice(512, 12, replace=False).tolist())
     print(_sampled_check(w, "mixed_8b", prefill_ids=[0, 3], decode_ids=ids))
+
+
+@pytest.mark.parametrize("shape", [workloads.AttnShape(16, 8, 128, 256), workloads.AttnShape(12, 4, 128, 16),
+                                   workloads.AttnShape(32, 8, 128, 64), workloads.AttnShape(8, 8, 128, 48)],
+                         ids=lambda s: f"{s.num_heads}q{s.num_kv_heads}kv_bs{s.block_size}")
+def test_long_prefix_short_chunks(shape):
+    """Chunks much shorter than their cached prefix: the launch takes the 8-wave workgroups
+    (max_seqlen_k >= 2 max_seqlen_q), including ragged q tails and odd group sizes."""
+    w = workloads.random_workload(300 + shape.num_heads, shape, n_prefill=5, n_decode=0,
+                                  max_len=150, max_cached=1500, share_prefix=True)
+    st = w.steps[0]
+    assert max(s.num_cached + s.num_new for s in st.prefill) >= 2 * max(s.num_new for s in st.prefill)
+    print(_full_check(w, f"long prefix {shape}"))

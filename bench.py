@@ -54,16 +54,54 @@ def source_hash(path: str) -> str:
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def load_traffic(kernel_src: str, per_launch_alg: float):
-    """HBM traffic of the decode kernel from the committed rocprofv3 counter summary, if it was
-    taken on the current source; otherwise None."""
-    path = os.path.join(ROOT, "profiles", "decode_traffic.json")
-    if not os.path.exists(path):
+DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_store_amd", "csrc", "decode.hip")
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "decode_traffic.json")
+CALIB_ELEMS = 1 << 28  # int32 elements of the counter-calibration op (1 GiB read, 1 GiB written)
+
+
+def load_traffic():
+    """HBM bytes per decode call (split + combine kernels) from the committed counter summary,
+    if it was taken on the current kernel source; otherwise None."""
+    if not os.path.exists(TRAFFIC_JSON):
         return None
-    rec = json.load(open(path))
-    if rec.get("source_sha256_16") != source_hash(kernel_src):
+    rec = json.load(open(TRAFFIC_JSON))
+    if rec.get("source_sha256_16") != source_hash(DECODE_SRC):
         return None
     return rec.get("bytes_per_launch")
+
+
+def traffic_from_counters(fetch_csv: str, write_csv: str) -> dict:
+    """Calibrated HBM traffic of the decode call from two rocprofv3 counter runs of
+    `bench.py --calibrate-copy` (one with --pmc FETCH_SIZE, one with --pmc WRITE_SIZE).
+
+    Each counter (KiB per dispatch) is scaled by the ratio of the true bytes to what the same
+    counter reports for the calibration op, a bitwise NOT over CALIB_ELEMS int32 values that
+    reads and writes exactly 4 * CALIB_ELEMS bytes."""
+    import csv
+    import statistics
+
+    def per_kernel(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            key = ("calib" if "bitwise_not" in name else
+                   "split" if "decode_split_kernel" in name else
+                   "combine" if "decode_combine_kernel" in name else None)
+            if key:
+                vals.setdefault(key, []).append(float(r["Counter_Value"]) * 1024.0)
+        return {k: statistics.median(v) for k, v in vals.items()}
+
+    f = per_kernel(fetch_csv, "FETCH_SIZE")
+    w = per_kernel(write_csv, "WRITE_SIZE")
+    true_bytes = 4.0 * CALIB_ELEMS
+    ff, wf = true_bytes / f["calib"], true_bytes / w["calib"]
+    fetch = ff * (f["split"] + f.get("combine", 0.0))
+    write = wf * (w["split"] + w.get("combine", 0.0))
+    return {"source_sha256_16": source_hash(DECODE_SRC), "fetch_factor": round(ff, 4),
+            "write_factor": round(wf, 4), "fetch_bytes_per_launch": round(fetch),
+            "write_bytes_per_launch": round(write), "bytes_per_launch": round(fetch + write)}
 
 
 def cpu_baseline(shape, ds, k_cache, v_cache, scale):
@@ -92,7 +130,18 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixed_8b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run the counter-calibration op (1 GiB bitwise NOT) before timing")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the decode call's calibrated HBM traffic from two rocprofv3 "
+                         "--pmc runs of --calibrate-copy to profiles/decode_traffic.json, exit")
     args = ap.parse_args()
+    if args.traffic:
+        rec = traffic_from_counters(*args.traffic)
+        rec["workload"] = args.workload
+        json.dump(rec, open(TRAFFIC_JSON, "w"), indent=1)
+        print(json.dumps(rec))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(this library has no multi-GPU path).", file=sys.stderr)
@@ -122,6 +171,13 @@ def main():
     pre_flops = sum(prefill_flops(shape, st.prefill) for st in w.steps)
     sto_bytes = sum(store_bytes(shape, ds.host["slot_mapping"]) for ds in dsteps)
 
+    if args.calibrate_copy:
+        x = torch.zeros(CALIB_ELEMS, dtype=torch.int32, device=dev)
+        y = torch.empty_like(x)
+        torch.bitwise_not(x, out=y)
+        torch.cuda.synchronize()
+        del x, y
+
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
         for ds in dsteps:
@@ -149,9 +205,7 @@ def main():
     dec_gbs = dec_bytes / (ms["decode"] * 1e-3) / 1e9 if dec_bytes else 0.0
     pre_tflops = pre_flops / (ms["prefill"] * 1e-3) / 1e12 if pre_flops else 0.0
     sto_gbs = sto_bytes / (ms["store"] * 1e-3) / 1e9
-    launches = max(1, sum(1 for ds in dsteps if "decode" in ds.host))
-    traffic = load_traffic(os.path.join(ROOT, "paged_kv_cache_store_amd", "csrc", "decode.hip"),
-                           dec_bytes / launches)
+    traffic = load_traffic()
 
     res = {
         "metric": "paged decode attn HBM GB/s (% peak); prefill attn TFLOP/s (% bf16 MFMA)",

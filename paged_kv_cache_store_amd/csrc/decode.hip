@@ -24,6 +24,9 @@
 //    second kernel merges the splits with the log-sum-exp rule:
 //    out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, M = max_s m_s.
 //  - Scores are kept in log2 units (scale * log2(e) folded in; exp2 is the hardware exp).
+//  - Grid order: the kv heads of one (sequence, split) are consecutive workgroups, so the
+//    G-head slices of the same pool rows are read at the same time (measured +9% on the
+//    Qwen3-8B decode over split-major order).
 // The split size depends only on host-known launch parameters: no device round trip.
 #include "nv_common.h"
 
@@ -37,6 +40,15 @@
 #ifndef NV_DECODE_TARGET_ITEMS
 #define NV_DECODE_TARGET_ITEMS 4096  // work items the split size aims for
 #endif
+#ifndef NV_DECODE_PV_DOT2
+#define NV_DECODE_PV_DOT2 0     // P.V as bf16-pair dot products over two keys at a time
+#endif
+#ifndef NV_DECODE_LAZY_RESCALE
+#define NV_DECODE_LAZY_RESCALE 1  // skip the output rescale when no running max moved
+#endif
+#ifndef NV_DECODE_HEAD_MAJOR
+#define NV_DECODE_HEAD_MAJOR 1  // dispatch the kv heads of one (sequence, split) consecutively
+#endif
 #ifndef NV_DECODE_MIN_WAVES
 #define NV_DECODE_MIN_WAVES 1   // occupancy hint: waves per SIMD the register budget must allow
 #endif
@@ -45,6 +57,7 @@ namespace nvp {
 namespace {
 
 static_assert(NV_DECODE_CHUNK == 16 || NV_DECODE_CHUNK == 32, "chunk of 16 or 32 keys");
+static_assert(NV_DECODE_CHUNK % 8 == 0, "P.V pairs rows of a chunk");
 constexpr int kChunk = NV_DECODE_CHUNK;  // keys per wave iteration
 constexpr int kRowLoads = kChunk / 4;    // 16-byte loads per lane per chunk, per tensor
 constexpr int kMaxSplitKeys = 2048;
@@ -93,7 +106,11 @@ template <int G>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NV_DECODE_MIN_WAVES))) void decode_split_kernel(DecodeArgs a) {
     __shared__ DecodeSmem<G> sm;
 
+#if NV_DECODE_HEAD_MAJOR
+    const int g = blockIdx.x, s = blockIdx.y, b = blockIdx.z;
+#else
     const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+#endif
     const int L = a.context_lens[b];
     const int k0 = s * a.split_keys;
     if (k0 >= L) return;  // past this sequence's context (or a padding row)
@@ -189,6 +206,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NV_DECODE_M
             }
         }
         float alpha[G];
+        bool moved = false;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             float cm = sv[0][h];
@@ -197,6 +215,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NV_DECODE_M
             cm = fmaxf(cm, __shfl_xor(cm, 16));
             cm = fmaxf(cm, __shfl_xor(cm, 32));
             const float m_new = fmaxf(m_run[h], cm);
+            moved |= m_new != m_run[h];
             alpha[h] = fast_exp2((m_run[h] - m_new) * a.scale_log2);  // 0 on the first chunk
             m_run[h] = m_new;
             const float msc = m_new * a.scale_log2;
@@ -208,22 +227,50 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NV_DECODE_M
             }
             l_run[h] = l_run[h] * alpha[h] + ps;
         }
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][e] *= alpha[h];
-#pragma unroll
-        for (int i = 0; i < kRowLoads; ++i) {
-            float vf[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                vf[2 * e] = bf16lo(buf.v[i][e]);
-                vf[2 * e + 1] = bf16hi(buf.v[i][e]);
-            }
+        // alpha is exactly 1 wherever no max moved: the rescale is skipped when none did.
+        if (!NV_DECODE_LAZY_RESCALE || __any(moved)) {
 #pragma unroll
             for (int h = 0; h < G; ++h)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(sv[i][h], vf[e], acc[h][e]);
+                for (int e = 0; e < 8; ++e) acc[h][e] *= alpha[h];
+        }
+        if constexpr (NV_DECODE_PV_DOT2) {
+            // Two keys at a time: pack (v_i[e], v_{i+1}[e]) and (p_i, p_{i+1}) as bf16 pairs
+            // and accumulate their dot product in fp32 (p rounded to bf16, as for the MFMA
+            // P.V of prefill).
+#pragma unroll
+            for (int i = 0; i < kRowLoads; i += 2) {
+                uint32_t pp[G];
+#pragma unroll
+                for (int h = 0; h < G; ++h) pp[h] = pack_bf16(sv[i][h], sv[i + 1][h]);
+#pragma unroll
+                for (int wd = 0; wd < 4; ++wd) {
+                    const uint32_t x = buf.v[i][wd], y = buf.v[i + 1][wd];
+                    const uint32_t lo = (x & 0xffffu) | (y << 16);          // dim 2 wd
+                    const uint32_t hi = (x >> 16) | (y & 0xffff0000u);      // dim 2 wd + 1
+#pragma unroll
+                    for (int h = 0; h < G; ++h) {
+                        acc[h][2 * wd] = __builtin_amdgcn_fdot2_f32_bf16(
+                            as_bf16x2(lo), as_bf16x2(pp[h]), acc[h][2 * wd], false);
+                        acc[h][2 * wd + 1] = __builtin_amdgcn_fdot2_f32_bf16(
+                            as_bf16x2(hi), as_bf16x2(pp[h]), acc[h][2 * wd + 1], false);
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kRowLoads; ++i) {
+                float vf[8];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    vf[2 * e] = bf16lo(buf.v[i][e]);
+                    vf[2 * e + 1] = bf16hi(buf.v[i][e]);
+                }
+#pragma unroll
+                for (int h = 0; h < G; ++h)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(sv[i][h], vf[e], acc[h][e]);
+            }
         }
     };
 
@@ -320,8 +367,12 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
 
 template <int G>
 nv_status launch_decode(const DecodeArgs &a, int batch, hipStream_t stream) {
-    nv_status st = launch(decode_split_kernel<G>, dim3(a.max_splits, a.num_kv_heads, batch),
-                          dim3(256), 0, stream, a);
+#if NV_DECODE_HEAD_MAJOR
+    const dim3 grid(a.num_kv_heads, a.max_splits, batch);
+#else
+    const dim3 grid(a.max_splits, a.num_kv_heads, batch);
+#endif
+    nv_status st = launch(decode_split_kernel<G>, grid, dim3(256), 0, stream, a);
     if (st != NV_OK) return st;
     return launch(decode_combine_kernel, dim3(a.num_heads, batch), dim3(kHeadDim), 0, stream, a);
 }

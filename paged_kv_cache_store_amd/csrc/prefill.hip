@@ -13,9 +13,12 @@
 //    heads and rows the workgroup holds.
 //  - K/V are walked in tiles of 64 keys, copied from HBM straight into LDS with
 //    global_load_lds (16 bytes per lane, no staging registers) into two LDS stages: the next
-//    tile streams in while the current one is multiplied; one barrier per tile. Each thread
-//    looks up its own key's block in the table, so any block size works and padding entries
-//    are never read (keys past the tile's end re-read the last valid key, then get masked).
+//    tile streams in while the current one is multiplied; one barrier per tile. When the block
+//    size is a multiple of 64 a full tile lies inside one block: one table lookup per tile
+//    gives a scalar base address and each lane adds a fixed offset. Otherwise (and for the
+//    last, partial tile) each lane looks up its own key's block, so any block size works;
+//    padding entries are never read, and keys past the end re-read the last valid key (a
+//    stale row could hold NaN, which 0 x NaN would carry into O) before being masked.
 //  - LDS rows are 256 bytes, unpadded; bank conflicts are avoided by XOR-swizzling the 16-byte
 //    chunks of a row (K: chunk ^ (row % 16); V: chunk ^ 2 (row % 4)), applied on the global
 //    side since the copy places lane i's 16 bytes at 16 i.
@@ -30,11 +33,16 @@
 //    with ds_read_b64_tr_b16 (each 16-lane group turns 4 keys x 16 dims into one dim x 4
 //    keys per lane), two reads per MFMA.
 //  - Softmax in log2 units with the scale folded into one FMA before exp2; masking only on
-//    tiles the causal diagonal or the key end cuts; the output rescale is skipped when no row
-//    max moved.
-//  - Work items are ordered (sequence, kv head, head subgroup, q tile from last to first) and
-//    remapped so consecutive items land on the same XCD: workgroups that read the same K/V
-//    share that XCD's L2.
+//    tiles the causal diagonal or the key end cuts. The running max used for the exponent may
+//    lag the true one by a bounded slack (probabilities up to 2^slack), so the 64-register
+//    output rescale runs only when some row's max grows past it, typically once per row
+//    block instead of on most tiles; the max cancels between O and l, so the result is the
+//    same. Row sums are dot products of the packed bf16 probabilities with ones, i.e. the
+//    sums of exactly the values that multiply V.
+//  - Work is dealt to the 8 XCDs by (head subgroup, sequence, kv head) group, round-robin with
+//    the kv head fastest: with a multiple of 8 kv heads every workgroup reading one kv head's
+//    K/V shares an L2, and every XCD gets a share of every sequence (balanced under mixed
+//    prompt lengths). Within an XCD the q tiles that see the most keys start first.
 #include "nv_common.h"
 
 #include <type_traits>
@@ -47,6 +55,15 @@
 #endif
 #ifndef NV_PREFILL_STAGES
 #define NV_PREFILL_STAGES 2    // LDS stages of K/V tiles (2 or 3)
+#endif
+#ifndef NV_PREFILL_FASTCOPY
+#define NV_PREFILL_FASTCOPY 1  // whole-block tiles: scalar base address + fixed lane offsets
+#endif
+#ifndef NV_PREFILL_SLACK
+#define NV_PREFILL_SLACK 8.0f  // rescale only when a row max grows by more than this (log2 units)
+#endif
+#ifndef NV_PREFILL_DOT2SUM
+#define NV_PREFILL_DOT2SUM 1   // row sums from the packed bf16 probabilities (dot2 with ones)
 #endif
 
 #if NV_PREFILL_SETPRIO
@@ -81,6 +98,17 @@ __device__ __forceinline__ void copy16_to_lds(const void *src, void *lds_base) {
                  : "memory", "m0");
 }
 
+// Same copy with a wave-uniform 64-bit base address in SGPRs and a 32-bit per-lane byte
+// offset: no per-lane address arithmetic.
+__device__ __forceinline__ void copy16_to_lds_sbase(const void *sbase, uint32_t voff,
+                                                    void *lds_base) {
+    const uint32_t base = (uint32_t)(uintptr_t)lds_base;
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(base)), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+}
+
 // Waits until at most N of this wave's memory loads are outstanding and all its LDS accesses
 // are done (loads complete in order, so the older tile's copies have landed), then meets the
 // workgroup at a barrier. Unlike __syncthreads this does not drain the younger copies.
@@ -111,10 +139,12 @@ struct PrefillArgs {
     int32_t group;       // G
     int32_t block_size;
     int32_t bs_shift;
-    int32_t n_qtiles;
-    int32_t items;
-    int32_t items_per_xcd;
+    int32_t batch;
+    int32_t n_groups;        // head subgroups x sequences x kv heads
+    int32_t groups_per_xcd;
+    int32_t tile_in_block;  // block_size % 64 == 0: a 64-key tile never straddles two blocks
     float scale_log2;
+    float rescale_slack;    // raw-score growth of a row max tolerated without a rescale
 };
 
 template <int HPW, int kWaves>
@@ -128,26 +158,29 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(NV_
     __shared__ __attribute__((aligned(1024))) uint8_t v_lds[NS][kTileBytes];
     __shared__ int32_t tbl[kTableSlots];  // the sequence's first block ids, staged once
 
-    // XCD-aware remap: hardware hands consecutive workgroup ids to different XCDs; give each
-    // XCD a contiguous range of work items.
+    // Work decomposition. A group is one (head subgroup, sequence, kv head), numbered with the
+    // kv head fastest; group q runs on XCD q % 8 (the hardware deals consecutive workgroup ids
+    // round-robin to the 8 XCDs). Within an XCD the q tiles are issued by rank from the end of
+    // their sequence: the last tiles, which see the most keys, start first.
     const int bid = blockIdx.x;
-    const int item = (bid & 7) * a.items_per_xcd + (bid >> 3);
-    if (item >= a.items) return;
-    const int hsub_count = a.group / HPW;
-    const int qt = a.n_qtiles - 1 - item % a.n_qtiles;
-    int rest = item / a.n_qtiles;
-    const int hs = rest % hsub_count;
-    rest /= hsub_count;
-    const int g = rest % a.num_kv_heads;
-    const int b = rest / a.num_kv_heads;
+    const int slot = bid >> 3;
+    const int rank = slot / a.groups_per_xcd;
+    const int grp = (bid & 7) + 8 * (slot - rank * a.groups_per_xcd);
+    if (grp >= a.n_groups) return;
+    const int g = grp % a.num_kv_heads;
+    const int b = (grp / a.num_kv_heads) % a.batch;
+    const int hs = grp / (a.num_kv_heads * a.batch);
 
     const int q0 = a.cu_q[b];
     const int Lq = a.cu_q[b + 1] - q0;
-    if (qt * M >= Lq) return;
+    const int n_tiles_q = (Lq + M - 1) / M;
+    if (rank >= n_tiles_q) return;
+    const int qt = n_tiles_q - 1 - rank;
     const int Lk = a.cu_k[b + 1] - a.cu_k[b];
     const int P = Lk - Lq;
 
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in SGPRs
     const int col = lane & 31;  // query row within the wave's 32
     const int hg = lane >> 5;   // lane half
     const int h = g * a.group + hs * HPW + w / kWavesPerHead;
@@ -194,12 +227,43 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(NV_
     // Wave w, instruction j moves tile rows 16w + 4j .. +3 (1 KiB, contiguous in LDS); lane i
     // lands at 16 i: row 16w + 4j + i/16, chunk position i%16, i.e. logical chunk
     // position ^ swizzle(row) of that row.
+    constexpr int kRowsPerWave = kTileKeys / kWaves;
+    constexpr int kCopyGroups = kRowsPerWave / 4;
+    // Whole-block tiles: lane byte offsets from the tile's first pool row, fixed for the loop.
+    uint32_t koff[kCopyGroups], voff[kCopyGroups];
+    const uint32_t pool_row_bytes = (uint32_t)kv_row_stride * 2;
+#pragma unroll
+    for (int j = 0; j < kCopyGroups; ++j) {
+        const int r = kRowsPerWave * w + 4 * j + (lane >> 4);
+        koff[j] = (uint32_t)r * pool_row_bytes + 16 * k_chunk_pos(r, lane & 15);
+        voff[j] = (uint32_t)r * pool_row_bytes + 16 * v_chunk_pos(r, lane & 15);
+    }
     auto copy_tile = [&](int key0, auto stage) {
         constexpr int st = decltype(stage)::value;
         uint8_t *kl = k_lds[st];
         uint8_t *vl = v_lds[st];
+        if (NV_PREFILL_FASTCOPY && a.tile_in_block && key0 + kTileKeys <= kv_end) {
+            int lb, off0;
+            if (a.bs_shift >= 0) {
+                lb = key0 >> a.bs_shift;
+                off0 = key0 & (a.block_size - 1);
+            } else {
+                lb = key0 / a.block_size;
+                off0 = key0 - lb * a.block_size;
+            }
+            const int blk = __builtin_amdgcn_readfirstlane(tbl[lb]);
+            const int64_t elem0 = ((int64_t)blk * a.block_size + off0) * kv_row_stride +
+                                  (int64_t)g * kHeadDim;
+            const uint16_t *kb = a.k_cache + elem0;
+            const uint16_t *vb = a.v_cache + elem0;
+#pragma unroll
+            for (int j = 0; j < kCopyGroups; ++j) {
+                copy16_to_lds_sbase(kb, koff[j], &kl[(kRowsPerWave * w + 4 * j) * kRowBytes]);
+                copy16_to_lds_sbase(vb, voff[j], &vl[(kRowsPerWave * w + 4 * j) * kRowBytes]);
+            }
+            return;
+        }
         const int pos = lane & 15;
-        constexpr int kRowsPerWave = kTileKeys / kWaves;
 #pragma unroll
         for (int j = 0; j < kRowsPerWave / 4; ++j) {
             const int r = kRowsPerWave * w + 4 * j + (lane >> 4);
@@ -278,8 +342,12 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(NV_
 #pragma unroll
             for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[kb][i]);
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float m_new = fmaxf(m_run, tmax);  // finite: key 0 is visible to every row
-        if (__any(m_new != m_run)) {  // rescale only when some row's max moved
+        // Rescale only when some row's max grew by more than the slack: until then the stale
+        // max keeps every probability below 2^slack, far from fp32/bf16 overflow, and the
+        // result is unchanged because the max cancels between O and l. The first tile always
+        // rescales (m_run = -inf; key 0 is visible to every row, so tmax is finite).
+        const float m_new = fmaxf(m_run, tmax);
+        if (__any(tmax > m_run + a.rescale_slack)) {
             const float alpha = fast_exp2((m_run - m_new) * a.scale_log2);  // 0 on the first tile
             l_part *= alpha;
 #pragma unroll
@@ -289,16 +357,37 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(NV_
             m_run = m_new;
         }
         const float msc = m_run * a.scale_log2;
-        float psum = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float p = fast_exp2(fmaf(s[kb][i], a.scale_log2, -msc));
-                s[kb][i] = p;
-                psum += p;
-            }
-        l_part += psum;
+            for (int i = 0; i < 16; ++i) s[kb][i] = fast_exp2(fmaf(s[kb][i], a.scale_log2, -msc));
+        // P in bf16 (the B operand of the P.V products); word 4u + e holds keys of MFMA step u.
+        uint32_t pw[16];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                pw[4 * u + e] = pack_bf16(s[u >> 1][8 * (u & 1) + 2 * e],
+                                          s[u >> 1][8 * (u & 1) + 2 * e + 1]);
+#if NV_PREFILL_DOT2SUM
+        {
+            const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+            float psum = 0.f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                psum = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pw[e]), ones, psum, false);
+            l_part += psum;
+        }
+#else
+        {
+            float psum = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) psum += s[kb][i];
+            l_part += psum;
+        }
+#endif
 
         // ---- O^T += V^T P^T, 16 keys per MFMA step ----
         NV_PRIO_HI();
@@ -307,11 +396,8 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(NV_
         // address of lane vt is row 16u + 4hg + vt/4 (+8), dims 16 (vj & 1) + 4 (vt%4) .. +3.
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int kb = u >> 1, ib = 8 * (u & 1);
-            u32x4 pw;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) pw[e] = pack_bf16(s[kb][ib + 2 * e], s[kb][ib + 2 * e + 1]);
-            const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+            const u32x4 pu = {pw[4 * u], pw[4 * u + 1], pw[4 * u + 2], pw[4 * u + 3]};
+            const bf16x8 pb = __builtin_bit_cast(bf16x8, pu);
             const int ra = 16 * u + 4 * hg + (vt >> 2), rb = ra + 8;
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
@@ -355,13 +441,16 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(NV_
 template <int HPW, int kWaves>
 nv_status launch_prefill(PrefillArgs a, int batch, int max_seqlen_q, hipStream_t stream) {
     constexpr int M = 32 * kWaves / HPW;
-    a.n_qtiles = (max_seqlen_q + M - 1) / M;
-    const int64_t items = (int64_t)batch * a.num_kv_heads * (a.group / HPW) * a.n_qtiles;
-    if (items == 0) return NV_OK;
-    if (items > (int64_t)INT32_MAX / 2) return NV_ERR_UNSUPPORTED;
-    a.items = (int32_t)items;
-    a.items_per_xcd = (int32_t)((items + 7) / 8);
-    return launch(prefill_kernel<HPW, kWaves>, dim3(8 * a.items_per_xcd), dim3(64 * kWaves), 0,
+    const int64_t n_qtiles = (max_seqlen_q + M - 1) / M;
+    const int64_t groups = (int64_t)batch * a.num_kv_heads * (a.group / HPW);
+    const int64_t groups_per_xcd = (groups + 7) / 8;
+    const int64_t blocks = 8 * groups_per_xcd * n_qtiles;
+    if (blocks == 0) return NV_OK;
+    if (blocks > (int64_t)INT32_MAX) return NV_ERR_UNSUPPORTED;
+    a.batch = batch;
+    a.n_groups = (int32_t)groups;
+    a.groups_per_xcd = (int32_t)groups_per_xcd;
+    return launch(prefill_kernel<HPW, kWaves>, dim3((uint32_t)blocks), dim3(64 * kWaves), 0,
                   stream, a);
 }
 
@@ -398,6 +487,7 @@ extern "C" nv_status nv_paged_attn_prefill(const void *q, const void *k_cache,
     if (head_dim != kHeadDim) return NV_ERR_UNSUPPORTED;
     const int G = num_heads / num_kv_heads;
     if (G > 8) return NV_ERR_UNSUPPORTED;
+    if (num_kv_heads > 65536) return NV_ERR_UNSUPPORTED;  // 32-bit in-tile byte offsets
     if (((int64_t)max_seqlen_k + block_size - 1) / block_size > kTableSlots)
         return NV_ERR_UNSUPPORTED;  // the block-table prefix must fit the LDS staging area
     if (batch == 0 || max_seqlen_q == 0) return NV_OK;
@@ -419,7 +509,9 @@ extern "C" nv_status nv_paged_attn_prefill(const void *q, const void *k_cache,
     a.block_size = block_size;
     a.bs_shift = (block_size & (block_size - 1)) == 0 ? __builtin_ctz((unsigned)block_size) : -1;
     a.scale_log2 = softmax_scale * kLog2e;
-    a.n_qtiles = a.items = a.items_per_xcd = 0;
+    a.rescale_slack = NV_PREFILL_SLACK / a.scale_log2;
+    a.tile_in_block = block_size % kTileKeys == 0;
+    a.batch = a.n_groups = a.groups_per_xcd = 0;
     if (G % 2 == 0) return launch_prefill_sized<2>(a, batch, max_seqlen_q, max_seqlen_k, stream);
     return launch_prefill_sized<1>(a, batch, max_seqlen_q, max_seqlen_k, stream);
 }

@@ -50,29 +50,22 @@
 #ifndef NV_PREFILL_WAVES
 #define NV_PREFILL_WAVES 2  // register budget for this many waves per SIMD
 #endif
-#ifndef NV_PREFILL_SETPRIO
-#define NV_PREFILL_SETPRIO 0  // raise the wave priority while it issues MFMA groups
-#endif
-#ifndef NV_PREFILL_STAGES
-#define NV_PREFILL_STAGES 2    // LDS stages of K/V tiles (2 or 3)
-#endif
 #ifndef NV_PREFILL_FASTCOPY
 #define NV_PREFILL_FASTCOPY 1  // whole-block tiles: scalar base address + fixed lane offsets
+#endif
+#ifndef NV_PREFILL_KPF
+#define NV_PREFILL_KPF 3       // K fragments read this many dim-steps ahead of their products
+#endif
+#ifndef NV_PREFILL_SGB
+#define NV_PREFILL_SGB 1       // pin the read/product interleave with scheduling group barriers
+#endif
+#ifndef NV_PREFILL_VPF
+#define NV_PREFILL_VPF 1       // read the first P.V step's V fragments before the softmax
 #endif
 #ifndef NV_PREFILL_SLACK
 #define NV_PREFILL_SLACK 8.0f  // rescale only when a row max grows by more than this (log2 units)
 #endif
-#ifndef NV_PREFILL_DOT2SUM
-#define NV_PREFILL_DOT2SUM 1   // row sums from the packed bf16 probabilities (dot2 with ones)
-#endif
 
-#if NV_PREFILL_SETPRIO
-#define NV_PRIO_HI() __builtin_amdgcn_s_setprio(1)
-#define NV_PRIO_LO() __builtin_amdgcn_s_setprio(0)
-#else
-#define NV_PRIO_HI()
-#define NV_PRIO_LO()
-#endif
 
 namespace nvp {
 namespace {
@@ -151,11 +144,9 @@ template <int HPW, int kWaves>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(NV_PREFILL_WAVES))) void prefill_kernel(PrefillArgs a) {
     constexpr int kWavesPerHead = kWaves / HPW;
     constexpr int M = 32 * kWavesPerHead;  // rows per workgroup
-    // NS stages of K and V tiles (row-major, swizzled), 32 KiB per stage; the stage index is
-    // always a compile-time constant.
-    constexpr int NS = NV_PREFILL_STAGES;
-    __shared__ __attribute__((aligned(1024))) uint8_t k_lds[NS][kTileBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t v_lds[NS][kTileBytes];
+    // Two stages each of K and V tiles (row-major, swizzled), 16 KiB per tile.
+    __shared__ __attribute__((aligned(1024))) uint8_t k_lds[2][kTileBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t v_lds[2][kTileBytes];
     __shared__ int32_t tbl[kTableSlots];  // the sequence's first block ids, staged once
 
     // Work decomposition. A group is one (head subgroup, sequence, kv head), numbered with the
@@ -238,10 +229,9 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(NV_
         koff[j] = (uint32_t)r * pool_row_bytes + 16 * k_chunk_pos(r, lane & 15);
         voff[j] = (uint32_t)r * pool_row_bytes + 16 * v_chunk_pos(r, lane & 15);
     }
-    auto copy_tile = [&](int key0, auto stage) {
-        constexpr int st = decltype(stage)::value;
-        uint8_t *kl = k_lds[st];
-        uint8_t *vl = v_lds[st];
+    // Copies of one tile's K or V rows (wave w: rows kRowsPerWave w .. +kRowsPerWave) into dst.
+    auto copy_rows = [&](int key0, uint8_t *dst, const uint16_t *pool, const uint32_t *offs,
+                         bool is_v) {
         if (NV_PREFILL_FASTCOPY && a.tile_in_block && key0 + kTileKeys <= kv_end) {
             int lb, off0;
             if (a.bs_shift >= 0) {
@@ -252,28 +242,67 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(NV_
                 off0 = key0 - lb * a.block_size;
             }
             const int blk = __builtin_amdgcn_readfirstlane(tbl[lb]);
-            const int64_t elem0 = ((int64_t)blk * a.block_size + off0) * kv_row_stride +
-                                  (int64_t)g * kHeadDim;
-            const uint16_t *kb = a.k_cache + elem0;
-            const uint16_t *vb = a.v_cache + elem0;
+            const uint16_t *base = pool + ((int64_t)blk * a.block_size + off0) * kv_row_stride +
+                                   (int64_t)g * kHeadDim;
 #pragma unroll
-            for (int j = 0; j < kCopyGroups; ++j) {
-                copy16_to_lds_sbase(kb, koff[j], &kl[(kRowsPerWave * w + 4 * j) * kRowBytes]);
-                copy16_to_lds_sbase(vb, voff[j], &vl[(kRowsPerWave * w + 4 * j) * kRowBytes]);
-            }
+            for (int j = 0; j < kCopyGroups; ++j)
+                copy16_to_lds_sbase(base, offs[j], dst + (kRowsPerWave * w + 4 * j) * kRowBytes);
             return;
         }
         const int pos = lane & 15;
 #pragma unroll
-        for (int j = 0; j < kRowsPerWave / 4; ++j) {
+        for (int j = 0; j < kCopyGroups; ++j) {
             const int r = kRowsPerWave * w + 4 * j + (lane >> 4);
             const int key = min(key0 + r, kv_end - 1);  // past the end: a valid row, masked later
-            const int64_t row = key_row_staged(key);
-            const uint16_t *kg = a.k_cache + row * kv_row_stride + g * kHeadDim;
-            const uint16_t *vg = a.v_cache + row * kv_row_stride + g * kHeadDim;
-            copy16_to_lds(kg + 8 * k_chunk_pos(r, pos), &kl[(kRowsPerWave * w + 4 * j) * kRowBytes]);
-            copy16_to_lds(vg + 8 * v_chunk_pos(r, pos), &vl[(kRowsPerWave * w + 4 * j) * kRowBytes]);
+            const uint16_t *src = pool + key_row_staged(key) * kv_row_stride + g * kHeadDim;
+            const int c = is_v ? v_chunk_pos(r, pos) : k_chunk_pos(r, pos);
+            copy16_to_lds(src + 8 * c, dst + (kRowsPerWave * w + 4 * j) * kRowBytes);
         }
+    };
+    auto copy_k = [&](int t, int st) {
+        copy_rows(t * kTileKeys, k_lds[st], a.k_cache, koff, false);
+    };
+    auto copy_v = [&](int t, int st) {
+        copy_rows(t * kTileKeys, v_lds[st], a.v_cache, voff, true);
+    };
+
+    // ---- S^T = K Q^T for the tile in LDS at Ks: two 32-key blocks ----
+    auto scores = [&](const uint8_t *Ks, f32x16 (&sc)[2]) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sc[kb][i] = 0.f;
+        // K fragments are read NV_PREFILL_KPF dim-steps ahead of the products that use them.
+        bf16x8 kf[8][2];
+        auto load_k = [&](int kt) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const int r = kb * 32 + col;
+                kf[kt][kb] = *reinterpret_cast<const bf16x8 *>(
+                    Ks + r * kRowBytes + 16 * k_chunk_pos(r, 2 * kt + hg));
+            }
+        };
+#pragma unroll
+        for (int kt = 0; kt < NV_PREFILL_KPF; ++kt) load_k(kt);
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt) {
+            if (kt + NV_PREFILL_KPF < 8) load_k(kt + NV_PREFILL_KPF);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kt][kb], qreg[kt], sc[kb], 0,
+                                                                 0, 0);
+        }
+#if NV_PREFILL_SGB
+        // Keep that order in the instruction schedule: the first reads, then two products and
+        // the next two reads per dim-step, then the last products.
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * NV_PREFILL_KPF, 0);
+#pragma unroll
+        for (int i = 0; i < 8 - NV_PREFILL_KPF; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * NV_PREFILL_KPF, 0);
+#endif
     };
 
     f32x16 o[4];
@@ -281,51 +310,14 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(NV_
     for (int d = 0; d < 4; ++d)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[d][i] = 0.f;
-    float m_run = -INFINITY;  // running max of this lane's row, raw score units
+    float m_run = -INFINITY;  // running max of this lane's row (raw score units), may lag
     float l_part = 0.f;       // this lane's share of the row sum
 
-    // Copies in flight per thread per tile (loads complete in order).
-    constexpr int kCopiesPerTile = 2 * (kTileKeys / kWaves) / 4;
-    // Prologue: tiles 0 .. NS-2 start streaming in.
-    copy_tile(0, std::integral_constant<int, 0>{});
-    if constexpr (NS > 2) {
-        if (1 < n_tiles) copy_tile(kTileKeys, std::integral_constant<int, 1>{});
-    }
-
-    const int vt = lane & 15, vj = lane >> 4;  // lane in its 16-lane group, group index
-    // One tile: wait for its copies, publish it with a barrier (which also retires the stage
-    // of tile t-1), start copying tile t + NS - 1 into that stage, multiply tile t.
-    auto tile_step = [&](int t, auto stage) {
-        constexpr int st = decltype(stage)::value;
+    // ---- mask (only tiles the diagonal or the key end cuts), row max, rare rescale ----
+    // Row i of the wave sees keys < P + r0 + i + 1; the whole tile is visible to every row of
+    // the wave when its last key is <= P + r0 (and below Lk).
+    auto mask_and_max = [&](int t, f32x16 (&sc)[2]) {
         const int key0 = t * kTileKeys;
-        if (NS > 2 && t + 1 < n_tiles) wait_copies_and_barrier<kCopiesPerTile>();
-        else wait_copies_and_barrier<0>();
-        if (t + NS - 1 < n_tiles)
-            copy_tile(key0 + (NS - 1) * kTileKeys,
-                      std::integral_constant<int, (st + NS - 1) % NS>{});
-        const uint8_t *Ks = k_lds[st];
-        const uint8_t *Vs = v_lds[st];
-
-        // ---- S^T = K Q^T for two 32-key blocks ----
-        NV_PRIO_HI();
-        f32x16 s[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-            const int r = kb * 32 + col;
-#pragma unroll
-            for (int kt = 0; kt < 8; ++kt) {
-                const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(
-                    Ks + r * kRowBytes + 16 * k_chunk_pos(r, 2 * kt + hg));
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[kt], s[kb], 0, 0, 0);
-            }
-        }
-
-        NV_PRIO_LO();
-        // ---- mask (only tiles the diagonal or the key end cuts), online softmax ----
-        // Row i of the wave sees keys < P + r0 + i + 1; the whole tile is visible to every
-        // row of the wave when its last key is <= P + r0 (and below Lk).
         if (key0 + kTileKeys - 1 > P + r0 || key0 + kTileKeys > Lk) {
             const int vis_end = min(Lk, P + my_row + 1);
 #pragma unroll
@@ -333,21 +325,21 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(NV_
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int j = key0 + kb * 32 + 8 * (i >> 2) + 4 * hg + (i & 3);
-                    if (j >= vis_end) s[kb][i] = -INFINITY;
+                    if (j >= vis_end) sc[kb][i] = -INFINITY;
                 }
         }
-        float tmax = s[0][0];
+        float tmax = sc[0][0];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[kb][i]);
+            for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sc[kb][i]);
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
         // Rescale only when some row's max grew by more than the slack: until then the stale
         // max keeps every probability below 2^slack, far from fp32/bf16 overflow, and the
         // result is unchanged because the max cancels between O and l. The first tile always
         // rescales (m_run = -inf; key 0 is visible to every row, so tmax is finite).
-        const float m_new = fmaxf(m_run, tmax);
         if (__any(tmax > m_run + a.rescale_slack)) {
+            const float m_new = fmaxf(m_run, tmax);
             const float alpha = fast_exp2((m_run - m_new) * a.scale_log2);  // 0 on the first tile
             l_part *= alpha;
 #pragma unroll
@@ -356,69 +348,88 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(NV_
                 for (int i = 0; i < 16; ++i) o[d][i] *= alpha;
             m_run = m_new;
         }
+    };
+
+    // ---- P = exp2(scale (S - m)) in bf16; word 4u + e holds keys of P.V step u ----
+    auto probs = [&](f32x16 (&sc)[2], uint32_t (&pw)[16]) {
         const float msc = m_run * a.scale_log2;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) s[kb][i] = fast_exp2(fmaf(s[kb][i], a.scale_log2, -msc));
-        // P in bf16 (the B operand of the P.V products); word 4u + e holds keys of MFMA step u.
-        uint32_t pw[16];
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                pw[4 * u + e] = pack_bf16(s[u >> 1][8 * (u & 1) + 2 * e],
-                                          s[u >> 1][8 * (u & 1) + 2 * e + 1]);
-#if NV_PREFILL_DOT2SUM
-        {
-            const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-            float psum = 0.f;
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-                psum = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pw[e]), ones, psum, false);
-            l_part += psum;
-        }
-#else
-        {
-            float psum = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) psum += s[kb][i];
-            l_part += psum;
-        }
-#endif
+            for (int e = 0; e < 4; ++e) {
+                const int kb = u >> 1, i = 8 * (u & 1) + 2 * e;
+                pw[4 * u + e] = pack_bf16(fast_exp2(fmaf(sc[kb][i], a.scale_log2, -msc)),
+                                          fast_exp2(fmaf(sc[kb][i + 1], a.scale_log2, -msc)));
+            }
+    };
 
-        // ---- O^T += V^T P^T, 16 keys per MFMA step ----
-        NV_PRIO_HI();
-        // V^T operand of lane (group vj, lane vt): dim 32 d + 16 (vj & 1) + vt, keys
-        // 16u + 4hg + {0..3} (first read) and 16u + 8 + 4hg + {0..3} (second read); the read
-        // address of lane vt is row 16u + 4hg + vt/4 (+8), dims 16 (vj & 1) + 4 (vt%4) .. +3.
+    // ---- O^T += V^T P^T for the tile in LDS at Vs, 16 keys per MFMA step; row sums ----
+    // V^T operand of lane (group vj, lane vt): dim 32 d + 16 (vj & 1) + vt, keys
+    // 16u + 4hg + {0..3} (first read) and 16u + 8 + 4hg + {0..3} (second read); the read
+    // address of lane vt is row 16u + 4hg + vt/4 (+8), dims 16 (vj & 1) + 4 (vt%4) .. +3.
+    const int vt = lane & 15, vj = lane >> 4;
+    // V^T fragments of P.V step u for the four 32-dim blocks.
+    auto load_v = [&](const uint8_t *Vs, int u, bf16x8 (&vf)[4]) {
+        const int ra = 16 * u + 4 * hg + (vt >> 2), rb = ra + 8;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const int dim = 32 * d + 16 * (vj & 1) + 4 * (vt & 3);
+            const int ca = v_chunk_pos(ra, dim >> 3), cb = v_chunk_pos(rb, dim >> 3);
+            const bf16x4v va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (NV_LDS bf16x4v *)(Vs + ra * kRowBytes + 16 * ca + 2 * (dim & 7)));
+            const bf16x4v vb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (NV_LDS bf16x4v *)(Vs + rb * kRowBytes + 16 * cb + 2 * (dim & 7)));
+            vf[d] = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+    };
+    // vf0: the fragments of step 0, read by the caller ahead of time.
+    auto pv = [&](const uint8_t *Vs, const uint32_t (&pw)[16], bf16x8 (&vf0)[4]) {
+        bf16x8 vf[4][4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) vf[0][d] = vf0[d];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
+            if (u + 1 < 4) load_v(Vs, u + 1, vf[u + 1]);
             const u32x4 pu = {pw[4 * u], pw[4 * u + 1], pw[4 * u + 2], pw[4 * u + 3]};
             const bf16x8 pb = __builtin_bit_cast(bf16x8, pu);
-            const int ra = 16 * u + 4 * hg + (vt >> 2), rb = ra + 8;
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                const int dim = 32 * d + 16 * (vj & 1) + 4 * (vt & 3);
-                const int ca = v_chunk_pos(ra, dim >> 3), cb = v_chunk_pos(rb, dim >> 3);
-                const bf16x4v va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                    (NV_LDS bf16x4v *)(Vs + ra * kRowBytes + 16 * ca + 2 * (dim & 7)));
-                const bf16x4v vb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                    (NV_LDS bf16x4v *)(Vs + rb * kRowBytes + 16 * cb + 2 * (dim & 7)));
-                const bf16x8 vw = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
-                o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vw, pb, o[d], 0, 0, 0);
-            }
+            for (int d = 0; d < 4; ++d)
+                o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[u][d], pb, o[d], 0, 0, 0);
         }
-        NV_PRIO_LO();
+        // Row sums of exactly the bf16 probabilities that multiplied V.
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+        float psum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            psum = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pw[e]), ones, psum, false);
+        l_part += psum;
     };
-    for (int t = 0; t < n_tiles; t += NS) {
-        tile_step(t, std::integral_constant<int, 0>{});
-        if (t + 1 < n_tiles) tile_step(t + 1, std::integral_constant<int, 1>{});
-        if constexpr (NS > 2) {
-            if (t + 2 < n_tiles) tile_step(t + 2, std::integral_constant<int, 2>{});
+
+    f32x16 sc[2];
+    // One tile per step: wait for its copies and publish it with a barrier (which also
+    // retires the other stage), start copying the next tile into the other stage, then
+    // scores, softmax and P.V of this one.
+    copy_k(0, 0);
+    copy_v(0, 0);
+    auto step = [&](int t, auto stage) {
+        constexpr int st = decltype(stage)::value;
+        wait_copies_and_barrier<0>();
+        if (t + 1 < n_tiles) {
+            copy_k(t + 1, st ^ 1);
+            copy_v(t + 1, st ^ 1);
         }
+        scores(k_lds[st], sc);
+        bf16x8 vf0[4];
+        if (NV_PREFILL_VPF) load_v(v_lds[st], 0, vf0);
+        mask_and_max(t, sc);
+        uint32_t pw[16];
+        probs(sc, pw);
+        if (!NV_PREFILL_VPF) load_v(v_lds[st], 0, vf0);
+        pv(v_lds[st], pw, vf0);
+    };
+    for (int t = 0; t < n_tiles; t += 2) {
+        step(t, std::integral_constant<int, 0>{});
+        if (t + 1 < n_tiles) step(t + 1, std::integral_constant<int, 1>{});
     }
 
     // ---- normalise and store: lane holds row `col`, dims 32d + 8(i/4) + 4hg + (i%4) ----

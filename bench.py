@@ -202,6 +202,26 @@ def main():
     wall = time.perf_counter() - t0
     ms = {n: sum(a.elapsed_time(b) for a, b in ev[n]) / args.steps for n in names}
 
+    # The same fresh prompts through the packed (no block table) prefill path, timed apart.
+    packed = [ds for ds in dsteps if ds.cu_seqlens_q is not None
+              and not ds.host["prefill"]["has_cached_context"]]
+    packed_ms = None
+    if packed:
+        for ds in packed:
+            gstep.run_prefill_packed(ds, scale)
+        pev = []
+        for _ in range(args.steps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for ds in packed:
+                gstep.run_prefill_packed(ds, scale)
+            b.record(stream)
+            pev.append((a, b))
+        torch.cuda.synchronize()
+        packed_ms = sum(a.elapsed_time(b) for a, b in pev) / args.steps
+        packed_flops = sum(prefill_flops(shape, ds.step.prefill) for ds in packed)
+
     dec_gbs = dec_bytes / (ms["decode"] * 1e-3) / 1e9 if dec_bytes else 0.0
     pre_tflops = pre_flops / (ms["prefill"] * 1e-3) / 1e12 if pre_flops else 0.0
     sto_gbs = sto_bytes / (ms["store"] * 1e-3) / 1e9
@@ -238,6 +258,11 @@ def main():
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
         "cpu_baseline": None,
     }
+    if packed_ms:
+        tf = packed_flops / (packed_ms * 1e-3) / 1e12
+        res["parts"]["prefill_packed"] = {"ms": round(packed_ms, 4), "TFLOP/s": round(tf, 1),
+                                          "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
+                                          "flops": packed_flops}
     if not args.no_cpu_baseline and dsteps[0].context_lens is not None:
         res["cpu_baseline"] = cpu_baseline(shape, dsteps[0], k_cache, v_cache, scale)
     print(json.dumps(res), flush=True)

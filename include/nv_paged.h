@@ -102,8 +102,10 @@ nv_status nv_store_kvcache(const void *key, int64_t key_row_stride,
  *   softmax_scale  positive and finite; the engine passes head_dim ** -0.5.
  *   out            device bf16 [total_q, num_heads, head_dim] contiguous; may not alias q.
  * Supported: head_dim == 128, num_heads % num_kv_heads == 0, (num_heads / num_kv_heads) <= 8,
- * block_size >= 1, ceil(max_seqlen_k / block_size) <= 2048. block_tables == NULL (the packed fresh-K/V mode of the engine's first
- * prefill) returns NV_ERR_UNSUPPORTED: store first, then attend through the table.
+ * block_size >= 1, ceil(max_seqlen_k / block_size) <= 2048.
+ * block_tables == NULL selects the packed fresh-K/V mode: k_cache/v_cache are then contiguous
+ * [total_k, num_kv_heads, head_dim] tensors and the call is nv_attn_prefill_packed with row
+ * strides num_kv_heads * head_dim (block_size and max_blocks_per_seq are ignored).
  * ------------------------------------------------------------------------------------------ */
 nv_status nv_paged_attn_prefill(const void *q, const void *k_cache, const void *v_cache,
                                 const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
@@ -112,6 +114,29 @@ nv_status nv_paged_attn_prefill(const void *q, const void *k_cache, const void *
                                 int32_t batch, int32_t num_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t block_size, float softmax_scale,
                                 void *out, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Prefill attention over packed fresh K/V ("Nano-vLLM Field Guide", Step 10.3: a prefill with
+ * no cached context attends over the freshly projected q, k, v, with cu_seqlens describing
+ * the packed sequences; Step 07.5 for cu_seqlens).
+ *
+ * Same operation and mask as nv_paged_attn_prefill, but key j of sequence b is row
+ * cu_seqlens_k[b] + j of k and v (no block table). In the engine's fresh prefill
+ * cu_seqlens_k == cu_seqlens_q; Lk_b >= Lq_b is the precondition in general.
+ *
+ *   k, v           device bf16 [total_k, num_kv_heads, head_dim], total_k = cu_seqlens_k[batch];
+ *                  the last two dims contiguous (heads head_dim apart).
+ *   k_row_stride / v_row_stride  elements between consecutive rows: >= num_kv_heads *
+ *                  head_dim and a multiple of 8 (v may be a view into the fused QKV output).
+ * Other arguments, layouts, limits and errors as for nv_paged_attn_prefill; additionally
+ * NV_ERR_INVALID_ARG for a bad stride.
+ * ------------------------------------------------------------------------------------------ */
+nv_status nv_attn_prefill_packed(const void *q, const void *k, int64_t k_row_stride,
+                                 const void *v, int64_t v_row_stride,
+                                 const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                                 int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t batch,
+                                 int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 float softmax_scale, void *out, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
  * Paged decode attention ("Nano-vLLM Field Guide", Step 10.3, decode; Step 07.6 for

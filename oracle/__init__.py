@@ -127,6 +127,26 @@ def attn_prefill(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, cu_seq
     return out
 
 
+def attn_prefill_packed(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_seqlens_q, cu_seqlens_k,
+                        num_heads: int, num_kv_heads: int, head_dim: int,
+                        scale: float) -> np.ndarray:
+    """Prefill with no cached context over packed fresh K/V ("Nano-vLLM Field Guide", Step
+    10.3: attention over the freshly projected q, k, v with cu_seqlens describing the packed
+    sequences). k, v: [total_k, Hkv*d] uint16 bf16 bits; key j of sequence b is row
+    cu_seqlens_k[b] + j. This is the paged computation with blocks of one token and a table
+    naming those rows, so it runs through the same code. Returns float64 [total_q, Hq, d]."""
+    ck = np.asarray(cu_seqlens_k, dtype=np.int64)
+    lens = ck[1:] - ck[:-1]
+    width = max(1, int(lens.max()) if len(lens) else 1)
+    table = np.full((len(lens), width), -1, dtype=np.int32)
+    for b, (start, n) in enumerate(zip(ck[:-1], lens)):
+        table[b, :n] = np.arange(start, start + n, dtype=np.int32)
+    k = np.ascontiguousarray(k, dtype=np.uint16)
+    v = np.ascontiguousarray(v, dtype=np.uint16)
+    return attn_prefill(q, k, v, cu_seqlens_q, cu_seqlens_k, table, num_heads, num_kv_heads,
+                        head_dim, 1, scale)
+
+
 def attn_decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, context_lens,
                 block_tables: np.ndarray, num_heads: int, num_kv_heads: int, head_dim: int,
                 block_size: int, scale: float) -> np.ndarray:

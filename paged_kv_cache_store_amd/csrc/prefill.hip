@@ -136,6 +136,8 @@ struct PrefillArgs {
     int32_t n_groups;        // head subgroups x sequences x kv heads
     int32_t groups_per_xcd;
     int32_t tile_in_block;  // block_size % 64 == 0: a 64-key tile never straddles two blocks
+    int64_t k_row_stride;   // elements between consecutive K rows (pool rows or packed rows)
+    int64_t v_row_stride;
     float scale_log2;
     float rescale_slack;    // raw-score growth of a row max tolerated without a rescale
 };
@@ -180,8 +182,10 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(NV_
     const int rows_hi = min(qt * M + M, Lq);
     const int kv_end = min(Lk, P + rows_hi);  // keys any row of this workgroup can see
     const int n_tiles = (kv_end + kTileKeys - 1) / kTileKeys;
-    const int32_t *table = a.block_tables + (int64_t)b * a.bt_width;
-    const int64_t kv_row_stride = (int64_t)a.num_kv_heads * kHeadDim;
+    // Packed mode (no block table): key j of sequence b is row cu_seqlens_k[b] + j of the
+    // packed K/V tensors.
+    const bool packed = a.block_tables == nullptr;
+    const int32_t *table = packed ? nullptr : a.block_tables + (int64_t)b * a.bt_width;
 
     // Q^T as the B operand: lane holds query row `col`, dims 16t + 8hg .. +8 for step t.
     bf16x8 qreg[8];
@@ -198,10 +202,14 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(NV_
     // Block ids of the keys this workgroup reads, staged in LDS so that no copy address waits
     // on a global load (the host guarantees they fit: ceil(max_seqlen_k / block_size) <=
     // kTableSlots).
-    const int n_blocks = a.bs_shift >= 0 ? (kv_end + a.block_size - 1) >> a.bs_shift
-                                         : (kv_end + a.block_size - 1) / a.block_size;
-    for (int i = tid; i < n_blocks; i += kWaves * 64) tbl[i] = table[i];
+    const int k_first = a.cu_k[b];
+    if (!packed) {
+        const int n_blocks = a.bs_shift >= 0 ? (kv_end + a.block_size - 1) >> a.bs_shift
+                                             : (kv_end + a.block_size - 1) / a.block_size;
+        for (int i = tid; i < n_blocks; i += kWaves * 64) tbl[i] = table[i];
+    }
     auto key_row_staged = [&](int j) -> int64_t {
+        if (packed) return (int64_t)k_first + j;
         int lb, off;
         if (a.bs_shift >= 0) {
             lb = j >> a.bs_shift;
@@ -222,28 +230,32 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(NV_
     constexpr int kCopyGroups = kRowsPerWave / 4;
     // Whole-block tiles: lane byte offsets from the tile's first pool row, fixed for the loop.
     uint32_t koff[kCopyGroups], voff[kCopyGroups];
-    const uint32_t pool_row_bytes = (uint32_t)kv_row_stride * 2;
 #pragma unroll
     for (int j = 0; j < kCopyGroups; ++j) {
         const int r = kRowsPerWave * w + 4 * j + (lane >> 4);
-        koff[j] = (uint32_t)r * pool_row_bytes + 16 * k_chunk_pos(r, lane & 15);
-        voff[j] = (uint32_t)r * pool_row_bytes + 16 * v_chunk_pos(r, lane & 15);
+        koff[j] = (uint32_t)(r * a.k_row_stride * 2) + 16 * k_chunk_pos(r, lane & 15);
+        voff[j] = (uint32_t)(r * a.v_row_stride * 2) + 16 * v_chunk_pos(r, lane & 15);
     }
     // Copies of one tile's K or V rows (wave w: rows kRowsPerWave w .. +kRowsPerWave) into dst.
     auto copy_rows = [&](int key0, uint8_t *dst, const uint16_t *pool, const uint32_t *offs,
                          bool is_v) {
-        if (NV_PREFILL_FASTCOPY && a.tile_in_block && key0 + kTileKeys <= kv_end) {
-            int lb, off0;
-            if (a.bs_shift >= 0) {
-                lb = key0 >> a.bs_shift;
-                off0 = key0 & (a.block_size - 1);
+        const int64_t row_stride = is_v ? a.v_row_stride : a.k_row_stride;
+        if (NV_PREFILL_FASTCOPY && (packed || a.tile_in_block) && key0 + kTileKeys <= kv_end) {
+            int64_t row0;
+            if (packed) {
+                row0 = (int64_t)k_first + key0;
             } else {
-                lb = key0 / a.block_size;
-                off0 = key0 - lb * a.block_size;
+                int lb, off0;
+                if (a.bs_shift >= 0) {
+                    lb = key0 >> a.bs_shift;
+                    off0 = key0 & (a.block_size - 1);
+                } else {
+                    lb = key0 / a.block_size;
+                    off0 = key0 - lb * a.block_size;
+                }
+                row0 = (int64_t)__builtin_amdgcn_readfirstlane(tbl[lb]) * a.block_size + off0;
             }
-            const int blk = __builtin_amdgcn_readfirstlane(tbl[lb]);
-            const uint16_t *base = pool + ((int64_t)blk * a.block_size + off0) * kv_row_stride +
-                                   (int64_t)g * kHeadDim;
+            const uint16_t *base = pool + row0 * row_stride + (int64_t)g * kHeadDim;
 #pragma unroll
             for (int j = 0; j < kCopyGroups; ++j)
                 copy16_to_lds_sbase(base, offs[j], dst + (kRowsPerWave * w + 4 * j) * kRowBytes);
@@ -254,7 +266,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(NV_
         for (int j = 0; j < kCopyGroups; ++j) {
             const int r = kRowsPerWave * w + 4 * j + (lane >> 4);
             const int key = min(key0 + r, kv_end - 1);  // past the end: a valid row, masked later
-            const uint16_t *src = pool + key_row_staged(key) * kv_row_stride + g * kHeadDim;
+            const uint16_t *src = pool + key_row_staged(key) * row_stride + g * kHeadDim;
             const int c = is_v ? v_chunk_pos(r, pos) : k_chunk_pos(r, pos);
             copy16_to_lds(src + 8 * c, dst + (kRowsPerWave * w + 4 * j) * kRowBytes);
         }
@@ -478,6 +490,69 @@ nv_status launch_prefill_sized(PrefillArgs a, int batch, int max_seqlen_q, int m
 }  // namespace
 }  // namespace nvp
 
+namespace nvp {
+namespace {
+
+// Checks shared by the paged and packed entry points, then the launch.
+nv_status prefill_checked(PrefillArgs a, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                          int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+                          int32_t head_dim, float softmax_scale, hipStream_t stream) {
+    if (batch < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_seqlen_q < 0 ||
+        max_seqlen_k < 0)
+        return NV_ERR_INVALID_ARG;
+    if (num_heads % num_kv_heads != 0) return NV_ERR_INVALID_ARG;
+    if (!(softmax_scale > 0.f) || softmax_scale == INFINITY) return NV_ERR_INVALID_ARG;
+    if (max_seqlen_q > max_seqlen_k) return NV_ERR_INVALID_ARG;
+    if (head_dim != kHeadDim) return NV_ERR_UNSUPPORTED;
+    const int G = num_heads / num_kv_heads;
+    if (G > 8) return NV_ERR_UNSUPPORTED;
+    if (num_kv_heads > 65536) return NV_ERR_UNSUPPORTED;  // 32-bit in-tile byte offsets
+    const int64_t min_stride = (int64_t)num_kv_heads * kHeadDim;
+    if (a.k_row_stride < min_stride || a.v_row_stride < min_stride) return NV_ERR_INVALID_ARG;
+    if (a.k_row_stride % 8 != 0 || a.v_row_stride % 8 != 0) return NV_ERR_INVALID_ARG;
+    if ((int64_t)kTileKeys * (a.k_row_stride > a.v_row_stride ? a.k_row_stride : a.v_row_stride) *
+            2 > (int64_t)UINT32_MAX)
+        return NV_ERR_UNSUPPORTED;  // in-tile byte offsets are 32-bit
+    if (batch == 0 || max_seqlen_q == 0) return NV_OK;
+    if (!a.q || !a.k_cache || !a.v_cache || !a.cu_q || !a.cu_k || !a.out)
+        return NV_ERR_INVALID_ARG;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.group = G;
+    a.scale_log2 = softmax_scale * kLog2e;
+    a.rescale_slack = NV_PREFILL_SLACK / a.scale_log2;
+    a.batch = a.n_groups = a.groups_per_xcd = 0;
+    if (G % 2 == 0) return launch_prefill_sized<2>(a, batch, max_seqlen_q, max_seqlen_k, stream);
+    return launch_prefill_sized<1>(a, batch, max_seqlen_q, max_seqlen_k, stream);
+}
+
+}  // namespace
+}  // namespace nvp
+
+extern "C" nv_status nv_attn_prefill_packed(const void *q, const void *k, int64_t k_row_stride,
+                                            const void *v, int64_t v_row_stride,
+                                            const int32_t *cu_seqlens_q,
+                                            const int32_t *cu_seqlens_k, int32_t max_seqlen_q,
+                                            int32_t max_seqlen_k, int32_t batch,
+                                            int32_t num_heads, int32_t num_kv_heads,
+                                            int32_t head_dim, float softmax_scale, void *out,
+                                            hipStream_t stream) {
+    using namespace nvp;
+    PrefillArgs a{};
+    a.q = static_cast<const uint16_t *>(q);
+    a.k_cache = static_cast<const uint16_t *>(k);
+    a.v_cache = static_cast<const uint16_t *>(v);
+    a.cu_q = cu_seqlens_q;
+    a.cu_k = cu_seqlens_k;
+    a.block_tables = nullptr;
+    a.out = static_cast<uint16_t *>(out);
+    a.bs_shift = -1;
+    a.k_row_stride = k_row_stride;
+    a.v_row_stride = v_row_stride;
+    return prefill_checked(a, max_seqlen_q, max_seqlen_k, batch, num_heads, num_kv_heads,
+                           head_dim, softmax_scale, stream);
+}
+
 extern "C" nv_status nv_paged_attn_prefill(const void *q, const void *k_cache,
                                            const void *v_cache, const int32_t *cu_seqlens_q,
                                            const int32_t *cu_seqlens_k, int32_t max_seqlen_q,
@@ -487,25 +562,18 @@ extern "C" nv_status nv_paged_attn_prefill(const void *q, const void *k_cache,
                                            int32_t head_dim, int32_t block_size,
                                            float softmax_scale, void *out, hipStream_t stream) {
     using namespace nvp;
-    if (batch < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
-        max_seqlen_q < 0 || max_seqlen_k < 0 || max_blocks_per_seq < 0)
-        return NV_ERR_INVALID_ARG;
-    if (num_heads % num_kv_heads != 0) return NV_ERR_INVALID_ARG;
-    if (!(softmax_scale > 0.f) || softmax_scale == INFINITY) return NV_ERR_INVALID_ARG;
-    if (max_seqlen_q > max_seqlen_k) return NV_ERR_INVALID_ARG;
+    if (num_kv_heads <= 0 || head_dim <= 0) return NV_ERR_INVALID_ARG;
+    const int64_t row = (int64_t)num_kv_heads * head_dim;
+    if (!block_tables)  // the engine's fresh-prompt path: contiguous packed K/V
+        return nv_attn_prefill_packed(q, k_cache, row, v_cache, row, cu_seqlens_q, cu_seqlens_k,
+                                      max_seqlen_q, max_seqlen_k, batch, num_heads,
+                                      num_kv_heads, head_dim, softmax_scale, out, stream);
+    if (block_size <= 0 || max_blocks_per_seq < 0 || max_seqlen_k < 0) return NV_ERR_INVALID_ARG;
     if ((int64_t)max_seqlen_k > (int64_t)max_blocks_per_seq * block_size)
         return NV_ERR_INVALID_ARG;
-    if (head_dim != kHeadDim) return NV_ERR_UNSUPPORTED;
-    const int G = num_heads / num_kv_heads;
-    if (G > 8) return NV_ERR_UNSUPPORTED;
-    if (num_kv_heads > 65536) return NV_ERR_UNSUPPORTED;  // 32-bit in-tile byte offsets
     if (((int64_t)max_seqlen_k + block_size - 1) / block_size > kTableSlots)
         return NV_ERR_UNSUPPORTED;  // the block-table prefix must fit the LDS staging area
-    if (batch == 0 || max_seqlen_q == 0) return NV_OK;
-    if (!block_tables) return NV_ERR_UNSUPPORTED;  // packed fresh-K/V mode not built
-    if (!q || !k_cache || !v_cache || !cu_seqlens_q || !cu_seqlens_k || !out)
-        return NV_ERR_INVALID_ARG;
-    PrefillArgs a;
+    PrefillArgs a{};
     a.q = static_cast<const uint16_t *>(q);
     a.k_cache = static_cast<const uint16_t *>(k_cache);
     a.v_cache = static_cast<const uint16_t *>(v_cache);
@@ -514,15 +582,10 @@ extern "C" nv_status nv_paged_attn_prefill(const void *q, const void *k_cache,
     a.block_tables = block_tables;
     a.out = static_cast<uint16_t *>(out);
     a.bt_width = max_blocks_per_seq;
-    a.num_heads = num_heads;
-    a.num_kv_heads = num_kv_heads;
-    a.group = G;
     a.block_size = block_size;
     a.bs_shift = (block_size & (block_size - 1)) == 0 ? __builtin_ctz((unsigned)block_size) : -1;
-    a.scale_log2 = softmax_scale * kLog2e;
-    a.rescale_slack = NV_PREFILL_SLACK / a.scale_log2;
     a.tile_in_block = block_size % kTileKeys == 0;
-    a.batch = a.n_groups = a.groups_per_xcd = 0;
-    if (G % 2 == 0) return launch_prefill_sized<2>(a, batch, max_seqlen_q, max_seqlen_k, stream);
-    return launch_prefill_sized<1>(a, batch, max_seqlen_q, max_seqlen_k, stream);
+    a.k_row_stride = a.v_row_stride = row;
+    return prefill_checked(a, max_seqlen_q, max_seqlen_k, batch, num_heads, num_kv_heads,
+                           head_dim, softmax_scale, stream);
 }

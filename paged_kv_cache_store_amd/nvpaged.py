@@ -21,6 +21,7 @@ if not os.path.exists(LIB_PATH):
                       "(or paged_kv_cache_store_amd/build.py) before using the HIP path")
 
 EXPORTS = ("nv_status_string", "nv_store_kvcache", "nv_paged_attn_prefill",
+           "nv_attn_prefill_packed",
            "nv_paged_attn_decode_workspace_size", "nv_paged_attn_decode",
            "nv_paged_attn_decode_split_keys", "nv_prepare_prefill", "nv_prepare_decode",
            "nv_check_indices")
@@ -39,6 +40,9 @@ def _bind(path: str) -> ctypes.CDLL:
     L.nv_paged_attn_prefill.argtypes = [_p, _p, _p, _p, _p, _i32, _i32, _p, _i32, _i32, _i32,
                                         _i32, _i32, _i32, _f32, _p, _p]
     L.nv_paged_attn_prefill.restype = ctypes.c_int
+    L.nv_attn_prefill_packed.argtypes = [_p, _p, _i64, _p, _i64, _p, _p, _i32, _i32, _i32, _i32,
+                                         _i32, _i32, _f32, _p, _p]
+    L.nv_attn_prefill_packed.restype = ctypes.c_int
     L.nv_paged_attn_decode_workspace_size.argtypes = [_i32] * 6
     L.nv_paged_attn_decode_workspace_size.restype = _sz
     L.nv_paged_attn_decode_split_keys.argtypes = [_i32] * 4
@@ -126,18 +130,7 @@ def nv_store_kvcache(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Tens
                                  n, hkv, d, ns, _stream(stream)), "nv_store_kvcache")
 
 
-def nv_paged_attn_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
-                          cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor,
-                          max_seqlen_q: int, max_seqlen_k: int, block_tables: torch.Tensor,
-                          num_kv_heads: int, block_size: int, softmax_scale: float,
-                          out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """q [total_q, Hq, d] bf16 contiguous -> out [total_q, Hq, d] bf16 (causal, bottom-right)."""
-    _dev(q, "q", torch.bfloat16)
-    if q.dim() != 3 or not q.is_contiguous():
-        raise ValueError("q must be a contiguous [total_q, num_heads, head_dim] tensor")
-    _, hq, d = q.shape
-    _pool_rows(k_cache, "k_cache", num_kv_heads * d)
-    _pool_rows(v_cache, "v_cache", num_kv_heads * d)
+def _cu_seqlens(cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor) -> int:
     for t, nm in ((cu_seqlens_q, "cu_seqlens_q"), (cu_seqlens_k, "cu_seqlens_k")):
         _dev(t, nm, torch.int32)
         if t.dim() != 1 or not t.is_contiguous():
@@ -145,6 +138,59 @@ def nv_paged_attn_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
     batch = cu_seqlens_q.numel() - 1
     if cu_seqlens_k.numel() != batch + 1:
         raise ValueError("cu_seqlens_q and cu_seqlens_k differ in length")
+    return batch
+
+
+def _q_out(q: torch.Tensor, out: torch.Tensor | None) -> torch.Tensor:
+    _dev(q, "q", torch.bfloat16)
+    if q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [total_q, num_heads, head_dim] tensor")
+    if out is None:
+        return torch.empty_like(q)
+    _dev(out, "out", torch.bfloat16)
+    if out.shape != q.shape or not out.is_contiguous():
+        raise ValueError("out must be contiguous and shaped like q")
+    return out
+
+
+def nv_attn_prefill_packed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                           cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor,
+                           max_seqlen_q: int, max_seqlen_k: int, softmax_scale: float,
+                           out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Causal varlen attention over packed fresh K/V: k, v [total_k, Hkv, d] bf16 (last two
+    dims contiguous, any row stride, e.g. views into a fused QKV output); sequence b's keys are
+    rows cu_seqlens_k[b] .. cu_seqlens_k[b+1]. q [total_q, Hq, d] -> out, bottom-right mask."""
+    out = _q_out(q, out)
+    _, hq, d = q.shape
+    for t, nm in ((k, "k"), (v, "v")):
+        _dev(t, nm, torch.bfloat16)
+        if t.dim() != 3 or t.stride(2) != 1 or t.stride(1) != d or t.shape[2] != d:
+            raise ValueError(f"{nm}: [total_k, num_kv_heads, head_dim] with the last two dims "
+                             "contiguous")
+    if v.shape != k.shape:
+        raise ValueError("k and v differ in shape")
+    batch = _cu_seqlens(cu_seqlens_q, cu_seqlens_k)
+    _check(_lib.nv_attn_prefill_packed(q.data_ptr(), k.data_ptr(), k.stride(0), v.data_ptr(),
+                                       v.stride(0), cu_seqlens_q.data_ptr(),
+                                       cu_seqlens_k.data_ptr(), int(max_seqlen_q),
+                                       int(max_seqlen_k), batch, hq, k.shape[1], d,
+                                       float(softmax_scale), out.data_ptr(), _stream(stream)),
+           "nv_attn_prefill_packed")
+    return out
+
+
+def nv_paged_attn_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                          cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor,
+                          max_seqlen_q: int, max_seqlen_k: int, block_tables: torch.Tensor,
+                          num_kv_heads: int, block_size: int, softmax_scale: float,
+                          out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """q [total_q, Hq, d] bf16 contiguous -> out [total_q, Hq, d] bf16 (causal, bottom-right).
+    block_tables None: k_cache/v_cache are contiguous packed fresh K/V [total_k, Hkv, d]."""
+    out = _q_out(q, out)
+    _, hq, d = q.shape
+    _pool_rows(k_cache, "k_cache", num_kv_heads * d)
+    _pool_rows(v_cache, "v_cache", num_kv_heads * d)
+    batch = _cu_seqlens(cu_seqlens_q, cu_seqlens_k)
     bt_ptr, width = 0, 0
     if block_tables is not None:
         _dev(block_tables, "block_tables", torch.int32)
@@ -152,12 +198,6 @@ def nv_paged_attn_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
                 not block_tables.is_contiguous():
             raise ValueError("block_tables must be a contiguous [batch, max_blocks] tensor")
         bt_ptr, width = block_tables.data_ptr(), block_tables.shape[1]
-    if out is None:
-        out = torch.empty_like(q)
-    else:
-        _dev(out, "out", torch.bfloat16)
-        if out.shape != q.shape or not out.is_contiguous():
-            raise ValueError("out must be contiguous and shaped like q")
     _check(_lib.nv_paged_attn_prefill(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                                       cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(),
                                       int(max_seqlen_q), int(max_seqlen_k), bt_ptr, width, batch,

@@ -84,6 +84,20 @@ def run_prefill(ds: DeviceStep, k_cache, v_cache, scale: float, stream=None) -> 
                                   out=ds.out_prefill, stream=stream)
 
 
+def run_prefill_packed(ds: DeviceStep, scale: float, stream=None) -> None:
+    """Prefill over the step's own fresh K/V rows, no block table (the engine's path when no
+    prompt has cached context); the prefill tokens are the step's first rows."""
+    if ds.cu_seqlens_q is None:
+        return
+    if ds.host["prefill"]["has_cached_context"]:
+        raise ValueError("packed prefill needs prompts without cached context")
+    t = ds.tensors
+    n = t.q_prefill.shape[0]
+    nvpaged.nv_attn_prefill_packed(t.q_prefill, t.key[:n], t.value[:n], ds.cu_seqlens_q,
+                                   ds.cu_seqlens_k, ds.max_seqlen_q, ds.max_seqlen_k, scale,
+                                   out=ds.out_prefill, stream=stream)
+
+
 def run_decode(ds: DeviceStep, k_cache, v_cache, scale: float, stream=None) -> None:
     if ds.context_lens is None:
         return

@@ -131,8 +131,17 @@ def test_device_calls_reject_bad_arguments_without_launch(nv):
     args = [1, 1, 1, 1, 1, 8, 8, 1, 1, 1]
     assert L.nv_paged_attn_prefill(*args, 6, 4, 128, 256, 0.1, 1, null) == -1
     assert L.nv_paged_attn_prefill(*args, 8, 4, 64, 256, 0.1, 1, null) == -2
-    assert L.nv_paged_attn_prefill(1, 1, 1, 1, 1, 8, 8, null, 1, 1, 8, 4, 128, 256, 0.1, 1,
-                                   null) == -2
+    # packed mode (no block table): row strides below one row or not a multiple of 8
+    assert L.nv_attn_prefill_packed(1, 1, 256, 1, 512, 1, 1, 8, 8, 1, 8, 4, 128, 0.1, 1,
+                                    null) == -1
+    assert L.nv_attn_prefill_packed(1, 1, 516, 1, 512, 1, 1, 8, 8, 1, 8, 4, 128, 0.1, 1,
+                                    null) == -1
+    assert L.nv_attn_prefill_packed(1, 1, 512, 1, 512, 1, 1, 9, 8, 1, 8, 4, 128, 0.1, 1,
+                                    null) == -1  # max_seqlen_q > max_seqlen_k
+    assert L.nv_attn_prefill_packed(null, null, 512, null, 512, null, null, 8, 8, 0, 8, 4, 128,
+                                    0.1, null, null) == 0  # empty batch
+    assert L.nv_paged_attn_prefill(1, 1, 1, 1, 1, 8, 8, null, 0, 1, 8, 4, 64, 0, 0.1, 1,
+                                   null) == -2  # packed mode, head_dim 64
     assert L.nv_paged_attn_prefill(1, 1, 1, 1, 1, 9, 8, 1, 1, 1, 8, 4, 128, 256, 0.1, 1,
                                    null) == -1  # max_seqlen_q > max_seqlen_k
     assert L.nv_paged_attn_prefill(1, 1, 1, 1, 1, 8, 300, 1, 1, 1, 8, 4, 128, 256, 0.1, 1,

@@ -239,3 +239,44 @@ def test_store_bit_copy_and_padding(oracle_lib):
     k3, v3 = k2.copy(), v2.copy()
     oracle.store_kvcache(key, value, k3, v3, sm)
     assert np.array_equal(k3, k2) and np.array_equal(v3, v2)
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"H{s.num_heads}/{s.num_kv_heads}d{s.head_dim}")
+def test_packed_prefill_matches_brute_force_and_paged(oracle_lib, shape):
+    """Packed fresh-K/V prefill (no block table): equals brute force on the packed rows and the
+    paged oracle on the same rows scattered into a permuted pool."""
+    rng = np.random.default_rng(31)
+    lq = np.array([5, 1, 17, 9])
+    lk = lq + np.array([0, 3, 0, 12])  # two fresh prompts, two with extra leading keys
+    cq = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    ck = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    D = shape.num_kv_heads * shape.head_dim
+    q = bits(torch.randn(int(cq[-1]), shape.num_heads, shape.head_dim).bfloat16())
+    k = bits(torch.randn(int(ck[-1]), D).bfloat16())
+    v = bits(torch.randn(int(ck[-1]), D).bfloat16())
+    scale = shape.head_dim ** -0.5
+    out = oracle.attn_prefill_packed(q, k, v, cq, ck, shape.num_heads, shape.num_kv_heads,
+                                     shape.head_dim, scale)
+    qf = bf16_bits_to_f64(q)
+    for b in range(len(lq)):
+        K = bf16_bits_to_f64(k[ck[b]:ck[b + 1]]).reshape(lk[b], shape.num_kv_heads, -1)
+        V = bf16_bits_to_f64(v[ck[b]:ck[b + 1]]).reshape(lk[b], shape.num_kv_heads, -1)
+        ref = brute_attention(qf[cq[b]:cq[b + 1]], K, V, scale, offset=int(lk[b] - lq[b]))
+        np.testing.assert_allclose(out[cq[b]:cq[b + 1]], ref, atol=1e-12, rtol=0)
+    # The same keys in a randomly permuted pool of blocks, read through block tables.
+    bs = 4
+    nblk = [-(-int(n) // bs) for n in lk]
+    perm = rng.permutation(sum(nblk) + 3)
+    kc = np.zeros((len(perm) * bs, D), np.uint16)
+    vc = np.zeros_like(kc)
+    table = np.full((len(lk), max(nblk)), -1, np.int32)
+    nxt = 0
+    for b in range(len(lk)):
+        table[b, :nblk[b]] = perm[nxt:nxt + nblk[b]]
+        nxt += nblk[b]
+        for j in range(lk[b]):
+            slot = table[b, j // bs] * bs + j % bs
+            kc[slot], vc[slot] = k[ck[b] + j], v[ck[b] + j]
+    paged = oracle.attn_prefill(q, kc, vc, cq, ck, table, shape.num_heads, shape.num_kv_heads,
+                                shape.head_dim, bs, scale)
+    np.testing.assert_array_equal(out, paged)

@@ -129,6 +129,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixed_8b")
+    ap.add_argument("--tp", type=int, default=1,
+                    help="run one rank's share of a tensor-parallel deployment of degree TP "
+                         "(heads divided by TP) on this one GPU")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run the counter-calibration op (1 GiB bitwise NOT) before timing")
@@ -154,7 +157,7 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = workloads.CONFIGS[args.workload]()
+    w = workloads.tp_share(workloads.CONFIGS[args.workload](), args.tp)
     shape = w.shape
     scale = shape.head_dim ** -0.5
     k_cache, v_cache, tens = workloads.materialize(w, dev, poison=False)
@@ -240,7 +243,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) bf16 values, randomly permuted physical blocks)",
-        "config": {"workload": w.name, "num_heads": shape.num_heads,
+        "config": {"workload": w.name, "tp_share": args.tp, "num_heads": shape.num_heads,
                    "num_kv_heads": shape.num_kv_heads, "head_dim": shape.head_dim,
                    "block_size": shape.block_size, "decode_seqs": len(w.steps[0].decode),
                    "prefill_tokens": w.steps[0].num_prefill_tokens, "seed": w.seed},

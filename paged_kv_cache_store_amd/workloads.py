@@ -205,6 +205,21 @@ def config_mixed_8b(seed: int = 1005) -> Workload:
                     num_blocks, pool.owned, [Step(prefill=prefill, decode=decode)], seed)
 
 
+def tp_share(w: Workload, tp: int) -> Workload:
+    """One rank's share of a workload under tensor parallelism of degree tp ("Nano-vLLM Field
+    Guide", Step 9.5: the query and kv head counts are divided by the tp size; Step 10.1: each
+    rank keeps its own cache of its heads). Sequences, block tables and seed are unchanged;
+    each rank's pool rows hold Hkv / tp heads."""
+    s = w.shape
+    if tp < 1 or s.num_heads % tp or s.num_kv_heads % tp:
+        raise ValueError(f"tp={tp} must divide {s.num_heads} q heads and {s.num_kv_heads} kv heads")
+    if tp == 1:
+        return w
+    shape = AttnShape(s.num_heads // tp, s.num_kv_heads // tp, s.head_dim, s.block_size)
+    return Workload(f"{w.name} [tp={tp}: one rank's heads]", shape, w.num_blocks, w.owned,
+                    w.steps, w.seed, w.note)
+
+
 CONFIGS = {
     "decode_small": config_decode_small,
     "prefill_varlen": config_prefill_varlen,

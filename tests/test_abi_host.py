@@ -182,3 +182,14 @@ def test_decode_split_choice(nv):
     assert nv.nv_paged_attn_decode_split_keys(4, 8, 4096, 1) <= 262
     # One split covers every context: no workspace needed.
     assert nv.nv_paged_attn_decode_workspace_size(4096, 16, 8, 128, 1, 256) == 0
+
+
+def test_tp_share_divides_heads_only():
+    w = workloads.config_mixed_8b()
+    r = workloads.tp_share(w, 4)
+    assert (r.shape.num_heads, r.shape.num_kv_heads) == (8, 2)
+    assert r.shape.head_dim == 128 and r.shape.block_size == w.shape.block_size
+    assert r.steps is w.steps and r.num_blocks == w.num_blocks
+    assert workloads.tp_share(w, 1) is w
+    with pytest.raises(ValueError):
+        workloads.tp_share(w, 3)

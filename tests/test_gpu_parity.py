@@ -140,3 +140,16 @@ def test_long_prefix_short_chunks(shape):
     st = w.steps[0]
     assert max(s.num_cached + s.num_new for s in st.prefill) >= 2 * max(s.num_new for s in st.prefill)
     print(_full_check(w, f"long prefix {shape}"))
+
+
+@pytest.mark.parametrize("tp", [2, 4, 8])
+@pytest.mark.parametrize("base", ["0.6b", "8b"])
+def test_tp_rank_shapes(tp, base):
+    """One rank's heads under tensor parallelism (q and kv heads divided by tp): store, prefill
+    with cached prefixes and decode at those shapes, full check against the oracle."""
+    shape = workloads.QWEN3_0_6B if base == "0.6b" else workloads.QWEN3_8B
+    w = workloads.random_workload(400 + tp, shape, n_prefill=3, n_decode=6, max_len=500,
+                                  max_cached=400, pad_rows=1, share_prefix=True)
+    w = workloads.tp_share(w, tp)
+    assert w.shape.num_heads == shape.num_heads // tp
+    print(_full_check(w, f"{base} tp={tp}"))

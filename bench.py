@@ -123,6 +123,55 @@ def cpu_baseline(shape, ds, k_cache, v_cache, scale):
                       f"{nbytes / 1e9:.2f} GB of K/V) in fp64 C, {dt:.1f} s"}
 
 
+def small_decode_latency(dev, iters: int, layers: int = 28) -> dict:
+    """Time of one small decode step (4 sequences + 2 padding rows, Qwen3-0.6B shape) through
+    `layers` attention layers, each with its own pool: store + decode launched eagerly per
+    layer vs one HIP-graph replay of all layers (inputs staged into the graph's static buffers
+    once per step). HIP events around each step; median."""
+    from paged_kv_cache_store_amd import graphs
+    from paged_kv_cache_store_amd import step as gstep
+    from paged_kv_cache_store_amd import workloads
+    w = workloads.CONFIGS["decode_small"]()
+    kc, vc, tens = workloads.materialize(w, dev)
+    ds = gstep.prepare_step(w.shape, w.steps[0], tens[0], dev)
+    scale = w.shape.head_dim ** -0.5
+    t = ds.tensors
+    ks = [kc] + [kc.clone() for _ in range(layers - 1)]
+    vs = [vc] + [vc.clone() for _ in range(layers - 1)]
+    dg = graphs.DecodeGraphs(w.shape, ks, vs, max_bs=8, max_blocks=ds.decode_tables.shape[1],
+                             scale=scale)
+    args = (t.q_decode, t.key, t.value, ds.slot_mapping, ds.context_lens, ds.decode_tables)
+
+    def eager():
+        for k_l, v_l in zip(ks, vs):
+            gstep.run_store(ds, k_l, v_l)
+            gstep.run_decode(ds, k_l, v_l, scale)
+
+    def replay():
+        dg.run(*args)
+
+    res = {"layers": layers}
+    for name, fn in (("eager_us", eager), ("graph_us", replay)):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        evs = []
+        for _ in range(iters):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        times = sorted(a.elapsed_time(b) for a, b in evs)
+        res[name] = round(times[len(times) // 2] * 1e3, 2)  # median, microseconds
+    res["rows"] = int(t.q_decode.shape[0])
+    res["bucket"] = dg.bucket_for(int(t.q_decode.shape[0]))
+    del dg, ks, vs
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -261,6 +310,7 @@ def main():
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
         "cpu_baseline": None,
     }
+    res["parts"]["decode_small_step"] = small_decode_latency(dev, max(20, args.steps))
     if packed_ms:
         tf = packed_flops / (packed_ms * 1e-3) / 1e12
         res["parts"]["prefill_packed"] = {"ms": round(packed_ms, 4), "TFLOP/s": round(tf, 1),

@@ -123,6 +123,45 @@ def cpu_baseline(shape, ds, k_cache, v_cache, scale):
                       f"{nbytes / 1e9:.2f} GB of K/V) in fp64 C, {dt:.1f} s"}
 
 
+def norm_rope_store_part(shape, dsteps, k_cache, v_cache, iters: int) -> dict:
+    """The step's rows through the fused per-head QK RMSNorm + rotary embedding + K/V store
+    (one launch per step), HIP events; algorithmic bytes: the projection rows read, q written,
+    K and V rows stored, positions and slots read (the 2 MiB rotary table is cache-resident and
+    not counted)."""
+    import torch as _t
+    from paged_kv_cache_store_amd import nvpaged
+    from paged_kv_cache_store_amd import step as gstep
+    dev = k_cache.device
+    g = _t.Generator(device="cpu").manual_seed(7)
+    wq = (1 + 0.1 * _t.randn(shape.head_dim, generator=g)).bfloat16().to(dev)
+    wk = (1 + 0.1 * _t.randn(shape.head_dim, generator=g)).bfloat16().to(dev)
+    table = nvpaged.rope_cos_sin_cache(40960, shape.head_dim, 1e6, dev)
+    nbytes = 0
+    for ds in dsteps:
+        n = ds.tensors.qkv.shape[0]
+        live = int((ds.host["slot_mapping"] != -1).sum())
+        nbytes += n * shape.qkv_width * 2 + n * shape.num_heads * shape.head_dim * 2 \
+            + live * 2 * shape.row_elems * 2 + n * 12
+    for _ in range(3):
+        for ds in dsteps:
+            gstep.run_norm_rope_store(ds, k_cache, v_cache, wq, wk, table)
+    _t.cuda.synchronize()
+    evs = []
+    for _ in range(iters):
+        a = _t.cuda.Event(enable_timing=True)
+        b = _t.cuda.Event(enable_timing=True)
+        a.record()
+        for ds in dsteps:
+            gstep.run_norm_rope_store(ds, k_cache, v_cache, wq, wk, table)
+        b.record()
+        evs.append((a, b))
+    _t.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in evs) / iters
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 4), "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "bytes": nbytes}
+
+
 def small_decode_latency(dev, iters: int, layers: int = 28) -> dict:
     """Time of one small decode step (4 sequences + 2 padding rows, Qwen3-0.6B shape) through
     `layers` attention layers, each with its own pool: store + decode launched eagerly per
@@ -310,6 +349,8 @@ def main():
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
         "cpu_baseline": None,
     }
+    res["parts"]["norm_rope_store"] = norm_rope_store_part(shape, dsteps, k_cache, v_cache,
+                                                           args.steps)
     res["parts"]["decode_small_step"] = small_decode_latency(dev, max(20, args.steps))
     if packed_ms:
         tf = packed_flops / (packed_ms * 1e-3) / 1e12

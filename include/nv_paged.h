@@ -139,6 +139,43 @@ nv_status nv_attn_prefill_packed(const void *q, const void *k, int64_t k_row_str
                                  float softmax_scale, void *out, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
+ * Fused per-head QK RMSNorm + rotary embedding + K/V store ("Nano-vLLM Field Guide", Step 9.5,
+ * Qwen3Attention.forward: q_norm / k_norm on every head, rotary_emb on q and k at the token's
+ * position, then store_kvcache; layernorm.py and rotary_embedding.py for the formulas).
+ *
+ * For token t, with its row of the fused projection output qkv[t] = [Hq q heads | Hkv k heads
+ * | Hkv v heads] of head_dim values each:
+ *   q and k heads x: n = bf16(x * rsqrt(mean(x^2) + eps)), y = bf16(n * w) (w = q_norm_weight
+ *   for q heads, k_norm_weight for k heads); then with y1, y2 the two halves of y and the
+ *   table row of positions[t]: out = [bf16(y1 cos - y2 sin), bf16(y2 cos + y1 sin)].
+ *   q results -> q_out[t]; k results -> k_out[t] (if k_out is not NULL) and to row
+ *   slot_mapping[t] of k_cache; v heads unchanged -> row slot_mapping[t] of v_cache.
+ *   A slot of -1 stores nothing (q_out and k_out are still written).
+ *
+ *   qkv            device bf16 [num_tokens, (Hq + 2 Hkv) head_dim] with row stride
+ *                  qkv_row_stride (elements, >= that width, multiple of 8).
+ *   positions      device int64 [num_tokens]; precondition 0 <= p < max_position (positions
+ *                  outside are clamped into the table).
+ *   q/k_norm_weight device bf16 [head_dim].
+ *   cos_sin_cache  device fp32 [max_position, head_dim]: row p holds cos(p theta_i) for
+ *                  i < head_dim/2, then sin(p theta_i) (the engine's table, theta_i =
+ *                  base^(-2i/head_dim)); read only.
+ *   eps            >= 0 (the engine uses 1e-6).
+ *   q_out          device bf16 [num_tokens, Hq, head_dim] contiguous.
+ *   k_out          device bf16 [num_tokens, Hkv, head_dim] contiguous, or NULL.
+ *   k_cache/v_cache/slot_mapping/num_slots  as for nv_store_kvcache.
+ * Supported: head_dim == 128, Hq % Hkv == 0. Errors: NV_ERR_INVALID_ARG (null pointer, bad
+ * sizes, stride or eps), NV_ERR_UNSUPPORTED (head_dim), NV_ERR_LAUNCH.
+ * ------------------------------------------------------------------------------------------ */
+nv_status nv_qk_norm_rope_store(const void *qkv, int64_t qkv_row_stride,
+                                const int64_t *positions, const void *q_norm_weight,
+                                const void *k_norm_weight, const float *cos_sin_cache,
+                                int64_t max_position, float eps, void *q_out, void *k_out,
+                                void *k_cache, void *v_cache, const int32_t *slot_mapping,
+                                int64_t num_tokens, int32_t num_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int64_t num_slots, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
  * Paged decode attention ("Nano-vLLM Field Guide", Step 10.3, decode; Step 07.6 for
  * context_lens; Step 07.8 for padding rows).
  *

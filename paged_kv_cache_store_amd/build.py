@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libnvpaged.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["store.hip", "decode.hip", "prefill.hip", "host_meta.cpp"]
+SOURCES = ["store.hip", "decode.hip", "prefill.hip", "norm_rope_store.hip", "host_meta.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC,

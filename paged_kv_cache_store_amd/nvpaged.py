@@ -21,7 +21,7 @@ if not os.path.exists(LIB_PATH):
                       "(or paged_kv_cache_store_amd/build.py) before using the HIP path")
 
 EXPORTS = ("nv_status_string", "nv_store_kvcache", "nv_paged_attn_prefill",
-           "nv_attn_prefill_packed",
+           "nv_attn_prefill_packed", "nv_qk_norm_rope_store",
            "nv_paged_attn_decode_workspace_size", "nv_paged_attn_decode",
            "nv_paged_attn_decode_split_keys", "nv_prepare_prefill", "nv_prepare_decode",
            "nv_check_indices")
@@ -43,6 +43,9 @@ def _bind(path: str) -> ctypes.CDLL:
     L.nv_attn_prefill_packed.argtypes = [_p, _p, _i64, _p, _i64, _p, _p, _i32, _i32, _i32, _i32,
                                          _i32, _i32, _f32, _p, _p]
     L.nv_attn_prefill_packed.restype = ctypes.c_int
+    L.nv_qk_norm_rope_store.argtypes = [_p, _i64, _p, _p, _p, _p, _i64, _f32, _p, _p, _p, _p,
+                                        _p, _i64, _i32, _i32, _i32, _i64, _p]
+    L.nv_qk_norm_rope_store.restype = ctypes.c_int
     L.nv_paged_attn_decode_workspace_size.argtypes = [_i32] * 6
     L.nv_paged_attn_decode_workspace_size.restype = _sz
     L.nv_paged_attn_decode_split_keys.argtypes = [_i32] * 4
@@ -177,6 +180,62 @@ def nv_attn_prefill_packed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                        float(softmax_scale), out.data_ptr(), _stream(stream)),
            "nv_attn_prefill_packed")
     return out
+
+
+def rope_cos_sin_cache(max_position: int, head_dim: int, base: float, device) -> torch.Tensor:
+    """The engine's rotary table, fp32 [max_position, head_dim]: row p = cos(p theta_i) for
+    i < head_dim/2, then sin(p theta_i), theta_i = base^(-2i/head_dim), computed in fp32 as the
+    engine does ("Nano-vLLM Field Guide", Step 9.5, rotary_embedding.py)."""
+    inv_freq = 1.0 / (base ** (torch.arange(0, head_dim, 2, dtype=torch.float) / head_dim))
+    t = torch.arange(max_position, dtype=torch.float)
+    freqs = torch.outer(t, inv_freq)
+    return torch.cat((freqs.cos(), freqs.sin()), dim=-1).to(device)
+
+
+def nv_qk_norm_rope_store(qkv: torch.Tensor, positions: torch.Tensor, q_norm_weight: torch.Tensor,
+                          k_norm_weight: torch.Tensor, cos_sin_cache: torch.Tensor, eps: float,
+                          k_cache: torch.Tensor, v_cache: torch.Tensor,
+                          slot_mapping: torch.Tensor, num_heads: int, num_kv_heads: int,
+                          q_out: torch.Tensor | None = None, want_k: bool = False,
+                          stream=None):
+    """qkv [N, (Hq + 2 Hkv) d] bf16 (last dim contiguous, any row stride): per-head RMSNorm and
+    rotary embedding of q and k, store of k and v at slot_mapping. Returns (q_out [N, Hq, d],
+    k_out [N, Hkv, d] or None)."""
+    _dev(qkv, "qkv", torch.bfloat16)
+    _dev(positions, "positions", torch.int64)
+    _dev(slot_mapping, "slot_mapping", torch.int32)
+    _dev(cos_sin_cache, "cos_sin_cache", torch.float32)
+    for t, nm in ((q_norm_weight, "q_norm_weight"), (k_norm_weight, "k_norm_weight")):
+        _dev(t, nm, torch.bfloat16)
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    if qkv.dim() != 2 or qkv.stride(1) != 1:
+        raise ValueError("qkv must be [num_tokens, width] with a contiguous last dim")
+    n = qkv.shape[0]
+    d = cos_sin_cache.shape[1]
+    if cos_sin_cache.dim() != 2 or not cos_sin_cache.is_contiguous():
+        raise ValueError("cos_sin_cache must be a contiguous [max_position, head_dim] tensor")
+    if qkv.shape[1] != (num_heads + 2 * num_kv_heads) * d:
+        raise ValueError("qkv width must be (num_heads + 2 num_kv_heads) * head_dim")
+    if positions.numel() != n or slot_mapping.numel() != n:
+        raise ValueError("positions and slot_mapping need one entry per token")
+    ns = _pool_rows(k_cache, "k_cache", num_kv_heads * d)
+    if _pool_rows(v_cache, "v_cache", num_kv_heads * d) != ns:
+        raise ValueError("k_cache and v_cache differ in size")
+    if q_out is None:
+        q_out = torch.empty(n, num_heads, d, dtype=torch.bfloat16, device=qkv.device)
+    k_out = (torch.empty(n, num_kv_heads, d, dtype=torch.bfloat16, device=qkv.device)
+             if want_k else None)
+    _check(_lib.nv_qk_norm_rope_store(qkv.data_ptr(), qkv.stride(0), positions.data_ptr(),
+                                      q_norm_weight.data_ptr(), k_norm_weight.data_ptr(),
+                                      cos_sin_cache.data_ptr(), cos_sin_cache.shape[0],
+                                      float(eps), q_out.data_ptr(),
+                                      k_out.data_ptr() if k_out is not None else None,
+                                      k_cache.data_ptr(), v_cache.data_ptr(),
+                                      slot_mapping.data_ptr(), n, int(num_heads),
+                                      int(num_kv_heads), d, ns, _stream(stream)),
+           "nv_qk_norm_rope_store")
+    return q_out, k_out
 
 
 def nv_paged_attn_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

@@ -33,8 +33,20 @@ class DeviceStep:
     decode_tables: Optional[torch.Tensor]
     workspace: Optional[torch.Tensor]
     host: dict                            # the host metadata, for checks and accounting
+    positions: Optional[torch.Tensor] = None  # int64 [N]: position of each row's token
     out_prefill: Optional[torch.Tensor] = None
     out_decode: Optional[torch.Tensor] = None
+
+
+def token_positions(step: Step) -> np.ndarray:
+    """Position of every row's token, prefill rows then decode rows: a prompt computes
+    positions num_cached .. num_cached + num_new - 1, a decode row its last position (0 for a
+    padding row)."""
+    parts = [np.arange(s.num_cached, s.num_cached + s.num_new, dtype=np.int64)
+             for s in step.prefill]
+    parts.append(np.array([max(s.num_cached + s.num_new - 1, 0) for s in step.decode],
+                          dtype=np.int64))
+    return np.concatenate(parts) if parts else np.zeros(0, np.int64)
 
 
 def prepare_step(shape: AttnShape, step: Step, tensors: StepTensors, device) -> DeviceStep:
@@ -60,8 +72,10 @@ def prepare_step(shape: AttnShape, step: Step, tensors: StepTensors, device) -> 
         ws = nvpaged.decode_workspace(tensors.q_decode, shape.num_kv_heads, dt, bs)
     sm = np.concatenate(slots) if slots else np.zeros(0, np.int32)
     host["slot_mapping"] = sm
+    host["positions"] = token_positions(step)
     ds = DeviceStep(shape, tensors, torch.from_numpy(sm).to(device), len(step.prefill), cu_q,
                     cu_k, mq, mk, pt, cl, dt, ws, host)
+    ds.positions = torch.from_numpy(host["positions"]).to(device)
     if step.prefill:
         ds.out_prefill = torch.empty_like(tensors.q_prefill)
     if step.decode:
@@ -82,6 +96,17 @@ def run_prefill(ds: DeviceStep, k_cache, v_cache, scale: float, stream=None) -> 
                                   ds.cu_seqlens_k, ds.max_seqlen_q, ds.max_seqlen_k,
                                   ds.prefill_tables, s.num_kv_heads, s.block_size, scale,
                                   out=ds.out_prefill, stream=stream)
+
+
+def run_norm_rope_store(ds: DeviceStep, k_cache, v_cache, q_norm_weight, k_norm_weight,
+                        cos_sin_cache, eps: float = 1e-6, stream=None):
+    """The step's rows through the fused per-head QK RMSNorm + rotary embedding + K/V store:
+    returns (q [N, Hq, d], k [N, Hkv, d]) normalised and rotated (k also stored)."""
+    s = ds.shape
+    return nvpaged.nv_qk_norm_rope_store(ds.tensors.qkv, ds.positions, q_norm_weight,
+                                         k_norm_weight, cos_sin_cache, eps, k_cache, v_cache,
+                                         ds.slot_mapping, s.num_heads, s.num_kv_heads,
+                                         want_k=True, stream=stream)
 
 
 def run_prefill_packed(ds: DeviceStep, scale: float, stream=None) -> None:

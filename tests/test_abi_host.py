@@ -193,3 +193,51 @@ def test_tp_share_divides_heads_only():
     assert workloads.tp_share(w, 1) is w
     with pytest.raises(ValueError):
         workloads.tp_share(w, 3)
+
+
+def test_norm_rope_store_rejects_bad_arguments_without_launch(nv):
+    L = nv.lib()
+    null = None
+    W = (16 + 2 * 8) * 128
+    base = [1, W, 1, 1, 1, 1, 4096, 1e-6, 1, null, 1, 1, 1, 4, 16, 8, 128, 64, null]
+    assert L.nv_qk_norm_rope_store(*base[:13], 0, *base[14:]) == 0  # no tokens
+    bad = list(base); bad[1] = W - 8
+    assert L.nv_qk_norm_rope_store(*bad) == -1  # row stride below the width
+    bad = list(base); bad[1] = W + 4
+    assert L.nv_qk_norm_rope_store(*bad) == -1  # row stride not a multiple of 8
+    bad = list(base); bad[16] = 64
+    assert L.nv_qk_norm_rope_store(*bad) == -2  # head_dim 64
+    bad = list(base); bad[7] = -1.0
+    assert L.nv_qk_norm_rope_store(*bad) == -1  # eps < 0
+    bad = list(base); bad[14], bad[15] = 6, 4
+    assert L.nv_qk_norm_rope_store(*bad) == -1  # q heads not a multiple of kv heads
+    bad = list(base); bad[6] = 0
+    assert L.nv_qk_norm_rope_store(*bad) == -1  # empty table
+    bad = list(base); bad[2] = null
+    assert L.nv_qk_norm_rope_store(*bad) == -1  # no positions
+
+
+def test_rope_table_follows_the_formula():
+    """The fp32 rotary table the binding builds against the oracle's float64 evaluation of the
+    same formula: differences come only from fp32 rounding of theta_i, of p * theta_i (at most
+    p * 2^-23 radians) and of cos/sin."""
+    from oracle import rope as R
+    from paged_kv_cache_store_amd import nvpaged as nvp
+    tab = nvp.rope_cos_sin_cache(4096, 128, 1e6, "cpu").double().numpy()
+    ref = R.rope_table_f64(4096, 128, 1e6)
+    p = np.arange(4096, dtype=np.float64)[:, None]
+    bound = p * 2.0 ** -22 + 2.0 ** -22
+    assert np.all(np.abs(tab - ref) <= bound)
+
+
+@pytest.mark.parametrize("name", list(workloads.CONFIGS))
+def test_token_positions_match_oracle(name):
+    from paged_kv_cache_store_amd import step as gstep
+    w = workloads.CONFIGS[name]()
+    for st in w.steps:
+        parts = []
+        if st.prefill:
+            parts.append(meta.prepare_prefill(st.prefill, w.shape.block_size)["positions"])
+        if st.decode:
+            parts.append(meta.prepare_decode(st.decode, w.shape.block_size)["positions"])
+        assert np.array_equal(gstep.token_positions(st), np.concatenate(parts))

@@ -73,9 +73,11 @@ def load_traffic():
     return rec.get("bytes_per_launch")
 
 
-def traffic_from_counters(fetch_csv: str, write_csv: str) -> dict:
+def traffic_from_counters(fetch_csv: str, write_csv: str, group: int) -> dict:
     """Calibrated HBM traffic of the decode call from two rocprofv3 counter runs of
-    `bench.py --calibrate-copy` (one with --pmc FETCH_SIZE, one with --pmc WRITE_SIZE).
+    `bench.py --calibrate-copy --step-only` (one with --pmc FETCH_SIZE, one with --pmc
+    WRITE_SIZE); `group` = q heads per kv head of the workload (the split kernel's template
+    argument).
 
     Each counter (KiB per dispatch) is scaled by the ratio of the true bytes to what the same
     counter reports for the calibration op, a bitwise NOT over CALIB_ELEMS int32 values that
@@ -90,7 +92,7 @@ def traffic_from_counters(fetch_csv: str, write_csv: str) -> dict:
                 continue
             name = r["Kernel_Name"]
             key = ("calib" if "bitwise_not" in name else
-                   "split" if "decode_split_kernel" in name else
+                   "split" if f"decode_split_kernel<{group}>" in name else
                    "combine" if "decode_combine_kernel" in name else None)
             if key:
                 vals.setdefault(key, []).append(float(r["Counter_Value"]) * 1024.0)
@@ -230,6 +232,8 @@ def main():
                     help="run one rank's share of a tensor-parallel deployment of degree TP "
                          "(heads divided by TP) on this one GPU")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--step-only", action="store_true",
+                    help="time only the step (store, prefill, decode): no extra parts")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run the counter-calibration op (1 GiB bitwise NOT) before timing")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -237,7 +241,9 @@ def main():
                          "--pmc runs of --calibrate-copy to profiles/decode_traffic.json, exit")
     args = ap.parse_args()
     if args.traffic:
-        rec = traffic_from_counters(*args.traffic)
+        from paged_kv_cache_store_amd import workloads as _w
+        s_ = _w.tp_share(_w.CONFIGS[args.workload](), args.tp).shape
+        rec = traffic_from_counters(*args.traffic, s_.num_heads // s_.num_kv_heads)
         rec["workload"] = args.workload
         json.dump(rec, open(TRAFFIC_JSON, "w"), indent=1)
         print(json.dumps(rec))
@@ -304,7 +310,7 @@ def main():
 
     # The same fresh prompts through the packed (no block table) prefill path, timed apart.
     packed = [ds for ds in dsteps if ds.cu_seqlens_q is not None
-              and not ds.host["prefill"]["has_cached_context"]]
+              and not ds.host["prefill"]["has_cached_context"] and not args.step_only]
     packed_ms = None
     if packed:
         for ds in packed:
@@ -358,9 +364,10 @@ def main():
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
         "cpu_baseline": None,
     }
-    res["parts"]["norm_rope_store"] = norm_rope_store_part(shape, dsteps, k_cache, v_cache,
-                                                           args.steps)
-    res["parts"]["decode_small_step"] = small_decode_latency(dev, max(20, args.steps))
+    if not args.step_only:
+        res["parts"]["norm_rope_store"] = norm_rope_store_part(shape, dsteps, k_cache, v_cache,
+                                                               args.steps)
+        res["parts"]["decode_small_step"] = small_decode_latency(dev, max(20, args.steps))
     if packed_ms:
         tf = packed_flops / (packed_ms * 1e-3) / 1e12
         res["parts"]["prefill_packed"] = {"ms": round(packed_ms, 4), "TFLOP/s": round(tf, 1),

@@ -16,9 +16,14 @@
 //    processed (two register buffers), 16 KiB per wave in flight.
 //  - Lane layout: 16 lanes x 16 B cover one 256-byte key (or value) row of the kv head, a wave
 //    covers 4 rows per load instruction. K . q is v_dot2_f32_bf16 (bf16 pairs, fp32 sum)
-//    followed by a DPP sum over the 16 lanes of the row; P.V is fp32 FMA with 8 output dims per
-//    lane. (Scores by a 16x16x32 bf16 MFMA with the query heads as columns were measured
-//    slower: the extra registers halve the waves per SIMD.)
+//    followed by a DPP sum over the 16 lanes of the row; P.V takes two keys at a time as
+//    v_dot2_f32_bf16 of (p_i, p_i+1) with (v_i, v_i+1), 8 output dims per lane, and the row
+//    sum adds the same bf16 probabilities. When a chunk lies inside one block, one table
+//    lookup gives a scalar base and each lane adds a fixed offset. The 8B shape (G = 4) is
+//    instruction-bound, so these cuts matter as long as the kernel keeps 3 waves per SIMD.
+//    (Scores by a 16x16x32 bf16 MFMA with the query heads as columns were measured slower:
+//    the extra registers halve the waves per SIMD.)
+//  - The running max may lag by a bounded slack, so the output rescale is rare.
 //  - At the end the 4 waves' (max, sum, output) are merged through LDS. A split's result is
 //    final when it is the sequence's only split; otherwise it goes to the workspace and a
 //    second kernel merges the splits with the log-sum-exp rule:
@@ -41,10 +46,10 @@
 #define NV_DECODE_TARGET_ITEMS 4096  // work items the split size aims for
 #endif
 #ifndef NV_DECODE_PV_DOT2
-#define NV_DECODE_PV_DOT2 0     // P.V as bf16-pair dot products over two keys at a time
+#define NV_DECODE_PV_DOT2 1     // P.V as bf16-pair dot products over two keys at a time
 #endif
-#ifndef NV_DECODE_LAZY_RESCALE
-#define NV_DECODE_LAZY_RESCALE 1  // skip the output rescale when no running max moved
+#ifndef NV_DECODE_SLACK
+#define NV_DECODE_SLACK 8.0f    // rescale only when a running max grows by more (log2 units)
 #endif
 #ifndef NV_DECODE_HEAD_MAJOR
 #define NV_DECODE_HEAD_MAJOR 1  // dispatch the kv heads of one (sequence, split) consecutively
@@ -81,6 +86,7 @@ struct DecodeArgs {
     int32_t split_keys;
     int32_t max_splits;
     float scale_log2;  // softmax_scale * log2(e)
+    float rescale_slack;  // raw-score growth of a running max tolerated without a rescale
 };
 
 struct Chunk {
@@ -102,8 +108,10 @@ struct DecodeSmem {
     float ml[4][G][2];
 };
 
+// Up to G = 4 the kernel fits 3 waves per SIMD (168 VGPRs) without spilling; the hint makes the
+// compiler hold that budget.
 template <int G>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NV_DECODE_MIN_WAVES))) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 : NV_DECODE_MIN_WAVES))) void decode_split_kernel(DecodeArgs a) {
     __shared__ DecodeSmem<G> sm;
 
 #if NV_DECODE_HEAD_MAJOR
@@ -156,8 +164,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NV_DECODE_M
     }
     __syncthreads();  // table slice visible
 
+    // Chunks inside one block (block size a multiple of the chunk, split aligned to it): one
+    // table lookup per chunk gives a scalar base, each lane adds a fixed 32-bit offset.
+    const bool chunk_in_block = (bs % kChunk) == 0 && (k0 % kChunk) == 0;
+    uint32_t lane_off[kRowLoads];
+#pragma unroll
+    for (int i = 0; i < kRowLoads; ++i)
+        lane_off[i] = (uint32_t)(((4 * i + sub) * rs + 8 * dc) * 2);
     auto load_chunk = [&](Chunk &buf, int ch) {
         const int kc = ch * kChunk;
+        if (chunk_in_block && kc + kChunk <= n) {
+            const int j = k0 + kc;
+            int lb, off;
+            if (a.bs_shift >= 0) {
+                lb = j >> a.bs_shift;
+                off = j & (bs - 1);
+            } else {
+                lb = j / bs;
+                off = j - lb * bs;
+            }
+            const int blk = __builtin_amdgcn_readfirstlane(sm.table[lb - lb0]);
+            const int64_t row0 = (int64_t)blk * bs + off;
+            const char *kp = reinterpret_cast<const char *>(kbase + row0 * rs);
+            const char *vp = reinterpret_cast<const char *>(vbase + row0 * rs);
+#pragma unroll
+            for (int i = 0; i < kRowLoads; ++i) {
+                buf.k[i] = NV_LOAD_STREAM(reinterpret_cast<const u32x4 *>(kp + lane_off[i]));
+                buf.v[i] = NV_LOAD_STREAM(reinterpret_cast<const u32x4 *>(vp + lane_off[i]));
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < kRowLoads; ++i) {
             const int jl = kc + 4 * i + sub;
@@ -205,36 +241,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NV_DECODE_M
                 sv[i][h] = ok ? d : -INFINITY;
             }
         }
-        float alpha[G];
-        bool moved = false;
+        // The running max may lag the true one by a bounded slack (probabilities up to
+        // 2^slack, far from overflow); the max cancels between numerator and sum, so the
+        // result is the same. The output rescale runs only when some head's max grows past
+        // the slack, typically a few times per split instead of on most chunks; the first
+        // chunk always rescales (m_run = -inf).
+        float cm[G];
+        bool grow = false;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            float cm = sv[0][h];
+            cm[h] = sv[0][h];
 #pragma unroll
-            for (int i = 1; i < kRowLoads; ++i) cm = fmaxf(cm, sv[i][h]);
-            cm = fmaxf(cm, __shfl_xor(cm, 16));
-            cm = fmaxf(cm, __shfl_xor(cm, 32));
-            const float m_new = fmaxf(m_run[h], cm);
-            moved |= m_new != m_run[h];
-            alpha[h] = fast_exp2((m_run[h] - m_new) * a.scale_log2);  // 0 on the first chunk
-            m_run[h] = m_new;
-            const float msc = m_new * a.scale_log2;
+            for (int i = 1; i < kRowLoads; ++i) cm[h] = fmaxf(cm[h], sv[i][h]);
+            cm[h] = fmaxf(cm[h], __shfl_xor(cm[h], 16));
+            cm[h] = fmaxf(cm[h], __shfl_xor(cm[h], 32));
+            grow |= cm[h] > m_run[h] + a.rescale_slack;
+        }
+        if (__any(grow)) {
+            asm volatile("");  // keeps the rescale a real branch (not if-converted)
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float m_new = fmaxf(m_run[h], cm[h]);
+                const float alpha = fast_exp2((m_run[h] - m_new) * a.scale_log2);
+                m_run[h] = m_new;
+                l_run[h] *= alpha;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float msc = m_run[h] * a.scale_log2;
             float ps = 0.f;
 #pragma unroll
             for (int i = 0; i < kRowLoads; ++i) {
                 sv[i][h] = fast_exp2(fmaf(sv[i][h], a.scale_log2, -msc));
-                ps += sv[i][h];
+                if constexpr (!NV_DECODE_PV_DOT2) ps += sv[i][h];
             }
-            l_run[h] = l_run[h] * alpha[h] + ps;
-        }
-        // alpha is exactly 1 wherever no max moved: the rescale is skipped when none did.
-        if (!NV_DECODE_LAZY_RESCALE || __any(moved)) {
-#pragma unroll
-            for (int h = 0; h < G; ++h)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[h][e] *= alpha[h];
+            if constexpr (!NV_DECODE_PV_DOT2) l_run[h] += ps;
         }
         if constexpr (NV_DECODE_PV_DOT2) {
+            const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
             // Two keys at a time: pack (v_i[e], v_{i+1}[e]) and (p_i, p_{i+1}) as bf16 pairs
             // and accumulate their dot product in fp32 (p rounded to bf16, as for the MFMA
             // P.V of prefill).
@@ -242,7 +289,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NV_DECODE_M
             for (int i = 0; i < kRowLoads; i += 2) {
                 uint32_t pp[G];
 #pragma unroll
-                for (int h = 0; h < G; ++h) pp[h] = pack_bf16(sv[i][h], sv[i + 1][h]);
+                for (int h = 0; h < G; ++h) {
+                    pp[h] = pack_bf16(sv[i][h], sv[i + 1][h]);
+                    // the sum takes exactly the bf16 probabilities that multiply V
+                    l_run[h] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pp[h]), ones, l_run[h],
+                                                               false);
+                }
 #pragma unroll
                 for (int wd = 0; wd < 4; ++wd) {
                     const uint32_t x = buf.v[i][wd], y = buf.v[i + 1][wd];
@@ -478,6 +530,7 @@ extern "C" nv_status nv_paged_attn_decode(const void *q, const void *k_cache,
     a.ws_o = need ? reinterpret_cast<float *>(static_cast<char *>(workspace) + ml_bytes)
                   : nullptr;
     a.scale_log2 = softmax_scale * kLog2e;
+    a.rescale_slack = NV_DECODE_SLACK / a.scale_log2;
     switch (G) {
         case 1: return launch_decode<1>(a, batch, stream);
         case 2: return launch_decode<2>(a, batch, stream);

@@ -24,6 +24,9 @@
 //    (Scores by a 16x16x32 bf16 MFMA with the query heads as columns were measured slower:
 //    the extra registers halve the waves per SIMD.)
 //  - The running max may lag by a bounded slack, so the output rescale is rare.
+//  - With G <= 4 the 16 lanes of a key row would all compute the same 4 G probabilities;
+//    instead each lane computes one, pairs it with the next row's (DPP rotate), and the bf16
+//    pairs are broadcast back to the row (DPP row_newbcast): one exp per lane and chunk.
 //  - At the end the 4 waves' (max, sum, output) are merged through LDS. A split's result is
 //    final when it is the sequence's only split; otherwise it goes to the workspace and a
 //    second kernel merges the splits with the log-sum-exp rule:
@@ -47,6 +50,9 @@
 #endif
 #ifndef NV_DECODE_PV_DOT2
 #define NV_DECODE_PV_DOT2 1     // P.V as bf16-pair dot products over two keys at a time
+#endif
+#ifndef NV_DECODE_EXPDEDUP
+#define NV_DECODE_EXPDEDUP 1    // G <= 4: one exp per lane, bf16 pairs broadcast back to the row
 #endif
 #ifndef NV_DECODE_SLACK
 #define NV_DECODE_SLACK 8.0f    // rescale only when a running max grows by more (log2 units)
@@ -100,6 +106,29 @@ struct Chunk {
 #else
 #define NV_LOAD_STREAM(ptr) (*(ptr))
 #endif
+
+// DPP within each 16-lane row: the value of lane kSrc in every lane (row_newbcast), and the
+// value of lane l - kBy (mod 16) in lane l (row_ror: a rotation towards higher lanes).
+template <int kSrc>
+__device__ __forceinline__ uint32_t row_bcast(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x150 + kSrc, 0xf, 0xf, false);
+}
+template <int kBy>
+__device__ __forceinline__ float row_ror(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + kBy, 0xf,
+                                                      0xf, false));
+}
+template <int G, int J, int H>
+__device__ __forceinline__ void bcast_pairs(uint32_t pk, uint32_t (&pp)[2][G]) {
+    if constexpr (J < 2) {
+        if constexpr (H < G) {
+            pp[J][H] = row_bcast<2 * J * G + H>(pk);
+            bcast_pairs<G, J, H + 1>(pk, pp);
+        } else {
+            bcast_pairs<G, J + 1, 0>(pk, pp);
+        }
+    }
+}
 
 template <int G>
 struct DecodeSmem {
@@ -227,7 +256,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
         float sv[kRowLoads][G];
 #pragma unroll
         for (int i = 0; i < kRowLoads; ++i) {
-            const bool ok = full || kc + 4 * i + sub < n;
 #pragma unroll
             for (int h = 0; h < G; ++h) {
                 float d = 0.f;
@@ -237,9 +265,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
                     d = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(kw), as_bf16x2(qp[h][e]), d,
                                                         false);
                 }
-                d = row16_sum(d);
-                sv[i][h] = ok ? d : -INFINITY;
+                sv[i][h] = row16_sum(d);
             }
+        }
+        if (!full) {  // only a split's last chunk has keys past its end
+            asm volatile("");  // keeps the masking a real branch (not if-converted)
+#pragma unroll
+            for (int i = 0; i < kRowLoads; ++i)
+#pragma unroll
+                for (int h = 0; h < G; ++h)
+                    if (kc + 4 * i + sub >= n) sv[i][h] = -INFINITY;
         }
         // The running max may lag the true one by a bounded slack (probabilities up to
         // 2^slack, far from overflow); the max cancels between numerator and sum, so the
@@ -268,6 +303,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
 #pragma unroll
                 for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
             }
+        }
+        // With G <= 4 the 16 lanes of a key row hold the same 4 G scores: lane dc computes
+        // only value dc = i G + h (row i, head h), pairs it with row i + 1 of the same head
+        // (lane dc + G) as bf16, and the pairs of even rows are broadcast back to the row.
+        constexpr bool kDedup = NV_DECODE_EXPDEDUP && NV_DECODE_PV_DOT2 && G <= 4 &&
+                                kRowLoads == 4;
+        if constexpr (kDedup) {
+            float sel = sv[0][0], msel = m_run[0];
+#pragma unroll
+            for (int i = 0; i < kRowLoads; ++i)
+#pragma unroll
+                for (int h = 0; h < G; ++h)
+                    if (i * G + h != 0) sel = dc == i * G + h ? sv[i][h] : sel;
+#pragma unroll
+            for (int h = 1; h < G; ++h) msel = dc % G == h ? m_run[h] : msel;
+            const float p = fast_exp2(fmaf(sel, a.scale_log2, -msel * a.scale_log2));
+            const uint32_t pk = pack_bf16(p, row_ror<16 - G>(p));  // with lane dc + G's value
+            uint32_t pp[2][G];
+            bcast_pairs<G, 0, 0>(pk, pp);
+            const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+#pragma unroll
+                for (int h = 0; h < G; ++h)
+                    l_run[h] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pp[j][h]), ones,
+                                                               l_run[h], false);
+#pragma unroll
+                for (int wd = 0; wd < 4; ++wd) {
+                    const uint32_t x = buf.v[2 * j][wd], y = buf.v[2 * j + 1][wd];
+                    const uint32_t lo = __builtin_amdgcn_perm(y, x, 0x05040100u);  // dim 2 wd
+                    const uint32_t hi = __builtin_amdgcn_perm(y, x, 0x07060302u);  // dim 2 wd + 1
+#pragma unroll
+                    for (int h = 0; h < G; ++h) {
+                        acc[h][2 * wd] = __builtin_amdgcn_fdot2_f32_bf16(
+                            as_bf16x2(lo), as_bf16x2(pp[j][h]), acc[h][2 * wd], false);
+                        acc[h][2 * wd + 1] = __builtin_amdgcn_fdot2_f32_bf16(
+                            as_bf16x2(hi), as_bf16x2(pp[j][h]), acc[h][2 * wd + 1], false);
+                    }
+                }
+            }
+            return;
         }
 #pragma unroll
         for (int h = 0; h < G; ++h) {

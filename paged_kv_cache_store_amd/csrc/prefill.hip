@@ -7,8 +7,9 @@
 // head; query head h reads kv head h / G.
 //
 // gfx950 design (bf16 MFMA, fp32 accumulation, online softmax):
-//  - A workgroup of W waves (4, or 8 when the context is long next to the new tokens) owns one
-//    kv head g, HPW query heads of its group and a tile of M = 32 W / HPW new rows; each wave
+//  - A workgroup of W waves owns one kv head g, HPW query heads of its group (4 when the group
+//    size allows, else 2 or 1) and a tile of M = 32 W / HPW new rows; W is 8 with four heads
+//    or when the context is long next to the new tokens, else 4. Each wave
 //    owns 32 rows of one head. Every K/V tile staged in LDS is therefore shared by all query
 //    heads and rows the workgroup holds.
 //  - K/V are walked in tiles of 64 keys, copied from HBM straight into LDS with
@@ -20,8 +21,8 @@
 //    padding entries are never read, and keys past the end re-read the last valid key (a
 //    stale row could hold NaN, which 0 x NaN would carry into O) before being masked.
 //  - LDS rows are 256 bytes, unpadded; bank conflicts are avoided by XOR-swizzling the 16-byte
-//    chunks of a row (K: chunk ^ (row % 16); V: chunk ^ 2 (row % 4)), applied on the global
-//    side since the copy places lane i's 16 bytes at 16 i.
+//    chunks of a row (K: chunk ^ (row % 16); V: chunk ^ 6 (row % 2) ^ 12 (row / 2 % 2)),
+//    applied on the global side since the copy places lane i's 16 bytes at 16 i.
 //  - Scores are computed transposed, S^T[key, row] = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //    K (A operand) is read from LDS, Q^T (B operand) stays in registers for the whole loop. In
 //    the 32x32 accumulator a lane holds one query row and 16 of its keys, so the softmax row
@@ -116,7 +117,13 @@ __device__ __forceinline__ void wait_copies_and_barrier() {
 
 // 16-byte chunk position of logical chunk c of tile row r in LDS.
 __device__ __forceinline__ int k_chunk_pos(int r, int c) { return c ^ (r & 15); }
-__device__ __forceinline__ int v_chunk_pos(int r, int c) { return c ^ ((r & 3) << 1); }
+// V rows are read four at a time by 16-lane groups (32 bytes of each row) and two such groups
+// (the other 32 bytes) are served together: the XOR pattern below gives the 4 rows x 4 chunks
+// 16 distinct chunk positions, and each group's 4 rows x 2 chunks 8 distinct positions modulo
+// 8, so neither read width hits a bank twice.
+__device__ __forceinline__ int v_chunk_pos(int r, int c) {
+    return c ^ ((r & 1) * 6) ^ (((r >> 1) & 1) * 12);
+}
 
 struct PrefillArgs {
     const uint16_t *q;
@@ -478,11 +485,13 @@ nv_status launch_prefill(PrefillArgs a, int batch, int max_seqlen_q, hipStream_t
 }
 
 // 8-wave workgroups (twice the query rows per K/V tile) pay off when each row sees a long
-// context: chunked or prefix-cached prefill. Fresh prompts keep 4 waves (more workgroups).
+// context: chunked or prefix-cached prefill. With two heads per workgroup, fresh prompts keep 4
+// waves (more workgroups); with four heads, 8 waves hold only 64 rows per head, so they are
+// taken for every prompt.
 template <int HPW>
 nv_status launch_prefill_sized(PrefillArgs a, int batch, int max_seqlen_q, int max_seqlen_k,
                                hipStream_t stream) {
-    if (max_seqlen_k >= 2 * max_seqlen_q)
+    if (HPW == 4 || max_seqlen_k >= 2 * max_seqlen_q)
         return launch_prefill<HPW, 8>(a, batch, max_seqlen_q, stream);
     return launch_prefill<HPW, 4>(a, batch, max_seqlen_q, stream);
 }
@@ -522,6 +531,7 @@ nv_status prefill_checked(PrefillArgs a, int32_t max_seqlen_q, int32_t max_seqle
     a.scale_log2 = softmax_scale * kLog2e;
     a.rescale_slack = NV_PREFILL_SLACK / a.scale_log2;
     a.batch = a.n_groups = a.groups_per_xcd = 0;
+    if (G % 4 == 0) return launch_prefill_sized<4>(a, batch, max_seqlen_q, max_seqlen_k, stream);
     if (G % 2 == 0) return launch_prefill_sized<2>(a, batch, max_seqlen_q, max_seqlen_k, stream);
     return launch_prefill_sized<1>(a, batch, max_seqlen_q, max_seqlen_k, stream);
 }

@@ -359,7 +359,7 @@ def main():
             "decode": {"ms": round(ms["decode"], 4), "GB/s": round(dec_gbs, 1),
                        "frac_hbm_peak": round(dec_gbs / HBM_PEAK_GBS, 4), "bytes": dec_bytes},
         },
-        "roofline": {"bound": "hbm", "kernel": "decode (split partial + combine)",
+        "roofline": {"bound": "hbm", "kernel": "decode (split kernel, + merge kernel when a row is split)",
                      "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
         "cpu_baseline": None,

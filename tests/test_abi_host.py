@@ -168,14 +168,16 @@ def test_device_calls_reject_bad_arguments_without_launch(nv):
 
 def test_decode_split_choice(nv):
     # Small batches get short splits so the chip fills; large ones get long splits (few
-    # partial results).
+    # partial results): 2048 (sequence, kv head) pairs or more run unsplit up to 8192 keys.
     assert nv.nv_paged_attn_decode_split_keys(6, 8, 3, 256) == 128
-    assert nv.nv_paged_attn_decode_split_keys(256, 8, 16, 256) == 2048
-    assert nv.nv_paged_attn_decode_split_keys(512, 8, 16, 256) == 2048
+    assert nv.nv_paged_attn_decode_split_keys(256, 8, 16, 256) == 8192
+    assert nv.nv_paged_attn_decode_split_keys(512, 8, 16, 256) == 8192
+    assert nv.nv_paged_attn_decode_split_keys(64, 8, 16, 256) == 1024  # 512 pairs x 4 splits
+    assert nv.nv_paged_attn_decode_workspace_size(512, 32, 8, 128, 16, 256) == 0
     prev = None
     for b in (1, 3, 17, 100, 600, 5000):
         s = nv.nv_paged_attn_decode_split_keys(b, 8, 16, 256)
-        assert s % 64 == 0 and 128 <= s <= 2048
+        assert s % 64 == 0 and 128 <= s <= 8192
         assert prev is None or s >= prev  # never shorter for a larger batch
         prev = s
     # Tiny blocks cap the split so one split's table slice fits the kernel's staging area.

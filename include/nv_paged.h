@@ -182,8 +182,10 @@ nv_status nv_qk_norm_rope_store(const void *qkv, int64_t qkv_row_stride,
  * One query row per sequence: out[b, h, :] = softmax(softmax_scale * q[b, h] K_b^T) V_b over
  * all context_lens[b] keys of sequence b (they include the token stored in this step). A row
  * with context_lens[b] == 0 (a padding row) attends to nothing and its output is zeros. The
- * key range of each sequence is split into chunks processed in parallel; the partial results
- * (max, sum, weighted values) are merged by a log-sum-exp combine.
+ * key range of each sequence may be split into chunks processed in parallel; the partial
+ * results (max, sum, weighted values) are then merged by a log-sum-exp combine. The split
+ * length depends only on batch, num_kv_heads, max_blocks_per_seq and block_size; when no row
+ * can span two splits the workspace size is 0 and a single kernel is launched.
  *
  *   q             device bf16 [batch, num_heads, head_dim] contiguous.
  *   context_lens  device int32 [batch], 0 <= context_lens[b] <= max_blocks_per_seq*block_size.

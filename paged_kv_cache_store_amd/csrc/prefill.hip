@@ -115,6 +115,14 @@ __device__ __forceinline__ void wait_copies_and_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// Waits until at most N of this wave's memory loads are outstanding (no LDS wait, no barrier).
+template <int N>
+__device__ __forceinline__ void wait_copies() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0xf << 8) | (0x7 << 4));
+    asm volatile("" ::: "memory");
+}
+
 // 16-byte chunk position of logical chunk c of tile row r in LDS.
 __device__ __forceinline__ int k_chunk_pos(int r, int c) { return c ^ (r & 15); }
 // V rows are read four at a time by 16-lane groups (32 bytes of each row) and two such groups
@@ -157,6 +165,11 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(NV_
     __shared__ __attribute__((aligned(1024))) uint8_t k_lds[2][kTileBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t v_lds[2][kTileBytes];
     __shared__ int32_t tbl[kTableSlots];  // the sequence's first block ids, staged once
+    // Query rows pass through LDS once, 8 KiB per wave: waves 0-3 use the second K/V stage
+    // (free until the second tile's copies, issued after everyone has read its queries),
+    // waves 4-7 a buffer of their own.
+    constexpr int kQWaveBytes = 32 * kRowBytes;
+    __shared__ __attribute__((aligned(1024))) uint8_t q_lds_hi[kWaves == 8 ? 4 * kQWaveBytes : 16];
 
     // Work decomposition. A group is one (head subgroup, sequence, kv head), numbered with the
     // kv head fastest; group q runs on XCD q % 8 (the hardware deals consecutive workgroup ids
@@ -194,17 +207,21 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(NV_
     const bool packed = a.block_tables == nullptr;
     const int32_t *table = packed ? nullptr : a.block_tables + (int64_t)b * a.bt_width;
 
-    // Q^T as the B operand: lane holds query row `col`, dims 16t + 8hg .. +8 for step t.
-    bf16x8 qreg[8];
-    {
-        const uint16_t *qp = a.q + ((int64_t)(q0 + my_row) * a.num_heads + h) * kHeadDim + 8 * hg;
+    // This wave's 32 query rows of head h, copied HBM -> LDS 4 rows per instruction (lane i:
+    // row 4j + i/16, chunk position i%16, K's swizzle), so every load covers whole rows. Rows
+    // past the sequence's end repeat its last row (their outputs are not stored).
+    uint8_t *q_slot = w < 2 ? k_lds[1] + w * kQWaveBytes
+                    : w < 4 ? v_lds[1] + (w - 2) * kQWaveBytes
+                            : q_lds_hi + (w - 4) * kQWaveBytes;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            u32x4 v = u32x4{0, 0, 0, 0};
-            if (my_row < Lq) v = *reinterpret_cast<const u32x4 *>(qp + 16 * t);
-            qreg[t] = __builtin_bit_cast(bf16x8, v);
-        }
+    for (int j = 0; j < 8; ++j) {
+        const int r = 4 * j + (lane >> 4);
+        const int row = min(r0 + r, Lq - 1);
+        const uint16_t *src = a.q + ((int64_t)(q0 + row) * a.num_heads + h) * kHeadDim +
+                              8 * k_chunk_pos(r, lane & 15);
+        copy16_to_lds(src, q_slot + 4 * j * kRowBytes);
     }
+    bf16x8 qreg[8];  // Q^T fragments, read from q_slot once the copies have landed
 
     // Block ids of the keys this workgroup reads, staged in LDS so that no copy address waits
     // on a global load (the host guarantees they fit: ceil(max_seqlen_k / block_size) <=
@@ -430,6 +447,13 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(NV_
     // scores, softmax and P.V of this one.
     copy_k(0, 0);
     copy_v(0, 0);
+    // Q^T as the B operand: lane holds query row `col`, dims 16t + 8hg .. +8 for step t. The
+    // query copies are this wave's oldest loads: wait until only the first tile's remain.
+    wait_copies<2 * kCopyGroups>();
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+        qreg[t] = *reinterpret_cast<const bf16x8 *>(q_slot + col * kRowBytes +
+                                                    16 * k_chunk_pos(col, 2 * t + hg));
     auto step = [&](int t, auto stage) {
         constexpr int st = decltype(stage)::value;
         wait_copies_and_barrier<0>();
@@ -452,20 +476,30 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(NV_
     }
 
     // ---- normalise and store: lane holds row `col`, dims 32d + 8(i/4) + 4hg + (i%4) ----
+    // Lanes l and l + 32 hold the two 4-dim halves of the same 8-dim groups. One
+    // v_permlane32_swap per word trades halves so that lane l ends with whole groups
+    // 8 (2rp + 1) .. +7 and lane l + 32 with groups 8 (2rp) .. +7 (rp = 0, 1): 16-byte stores
+    // instead of 8-byte ones.
     const float l_tot = l_part + __shfl_xor(l_part, 32);
-    if (my_row < Lq) {
-        const float inv = 1.f / l_tot;
-        uint16_t *op = a.out + ((int64_t)(q0 + my_row) * a.num_heads + h) * kHeadDim + 4 * hg;
+    const float inv = 1.f / l_tot;
+    uint16_t *op = a.out + ((int64_t)(q0 + my_row) * a.num_heads + h) * kHeadDim;
 #pragma unroll
-        for (int d = 0; d < 4; ++d)
+    for (int d = 0; d < 4; ++d)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                u32x2 pk;
-                pk[0] = pack_bf16(o[d][4 * r] * inv, o[d][4 * r + 1] * inv);
-                pk[1] = pack_bf16(o[d][4 * r + 2] * inv, o[d][4 * r + 3] * inv);
-                *reinterpret_cast<u32x2 *>(op + 32 * d + 8 * r) = pk;
-            }
-    }
+        for (int rp = 0; rp < 2; ++rp) {
+            const int ra = 2 * rp, rb = 2 * rp + 1;
+            const uint32_t a0 = pack_bf16(o[d][4 * ra] * inv, o[d][4 * ra + 1] * inv);
+            const uint32_t a1 = pack_bf16(o[d][4 * ra + 2] * inv, o[d][4 * ra + 3] * inv);
+            const uint32_t b0 = pack_bf16(o[d][4 * rb] * inv, o[d][4 * rb + 1] * inv);
+            const uint32_t b1 = pack_bf16(o[d][4 * rb + 2] * inv, o[d][4 * rb + 3] * inv);
+            // first result: lanes 0-31 keep b, lanes 32-63 get lanes 0-31's a;
+            // second result: lanes 0-31 get lanes 32-63's b, lanes 32-63 keep a
+            const auto s0 = __builtin_amdgcn_permlane32_swap(b0, a0, false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(b1, a1, false, false);
+            const u32x4 pk = {s0[0], s1[0], s0[1], s1[1]};
+            if (my_row < Lq)
+                *reinterpret_cast<u32x4 *>(op + 32 * d + 8 * (hg ? ra : rb)) = pk;
+        }
 }
 
 template <int HPW, int kWaves>

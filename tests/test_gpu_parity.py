@@ -109,6 +109,30 @@ def test_unsplit_decode_with_padding_rows():
     print(assert_attn_close(ds.out_decode[ids], ref, "unsplit decode"))
 
 
+@pytest.mark.parametrize("bs", [256, 16])
+def test_long_contexts_many_splits(bs):
+    """Few long decode rows: the split falls to the 128-key minimum (bs 256: ~160 splits per
+    row, all merged by the combine kernel) or is capped by the LDS table slice (bs 16), next to
+    a one-key row; plus a prefill chunk whose cached prefix fills ~2000 of the 2048 staged
+    table entries (bs 16)."""
+    from paged_kv_cache_store_amd import nvpaged
+    shape = workloads.AttnShape(16, 8, 128, bs)
+    rng = np.random.default_rng(77 + bs)
+    lens = [1, 20000, 9000]
+    pre = [(31960, 40)] if bs == 16 else [(4000, 70)]
+    need = sum(-(-L // bs) for L in lens) + sum(-(-(c + n) // bs) for c, n in pre) + 2
+    pool = workloads._Pool(need, rng)
+    prefill = [workloads.Seq(pool.take(-(-(c + n) // bs)), c, n) for c, n in pre]
+    decode = [workloads.Seq(pool.take(-(-L // bs)), L - 1, 1) for L in lens]
+    w = workloads.Workload(f"long contexts bs{bs}", shape, need, pool.owned,
+                           [workloads.Step(prefill=prefill, decode=decode)], 77)
+    width = -(-max(lens) // bs)
+    split = nvpaged.nv_paged_attn_decode_split_keys(len(lens), 8, width, bs)
+    print(f"[long] bs={bs}: decode split {split} keys, {-(-max(lens) // split)} splits", flush=True)
+    assert -(-max(lens) // split) >= 5
+    print(_full_check(w, f"long contexts bs{bs}"))
+
+
 def _sampled_check(w, label, prefill_ids=None, decode_ids=None):
     run = Run(w)
     stats = {}

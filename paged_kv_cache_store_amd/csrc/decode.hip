@@ -81,7 +81,10 @@ static_assert(NV_DECODE_CHUNK % 8 == 0, "P.V pairs rows of a chunk");
 constexpr int kChunk = NV_DECODE_CHUNK;  // keys per wave iteration
 constexpr int kRowLoads = kChunk / 4;    // 16-byte loads per lane per chunk, per tensor
 constexpr int kMaxSplitKeys = NV_DECODE_MAX_SPLIT;
-constexpr int kMinSplitKeys = 128;
+#ifndef NV_DECODE_MIN_SPLIT
+#define NV_DECODE_MIN_SPLIT 128
+#endif
+constexpr int kMinSplitKeys = NV_DECODE_MIN_SPLIT;
 constexpr int kTableSlots = 264;    // block ids of one split staged in LDS
 
 struct DecodeArgs {

@@ -76,8 +76,8 @@ def load_traffic():
 def traffic_from_counters(fetch_csv: str, write_csv: str, group: int) -> dict:
     """Calibrated HBM traffic of the decode call from two rocprofv3 counter runs of
     `bench.py --calibrate-copy --step-only` (one with --pmc FETCH_SIZE, one with --pmc
-    WRITE_SIZE); `group` = q heads per kv head of the workload (the split kernel's template
-    argument).
+    WRITE_SIZE); `group` = q heads per kv head of the workload (the split kernel's first
+    template argument; the second, false, selects the plain decode the step runs).
 
     Each counter (KiB per dispatch) is scaled by the ratio of the true bytes to what the same
     counter reports for the calibration op, a bitwise NOT over CALIB_ELEMS int32 values that
@@ -92,7 +92,7 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, group: int) -> dict:
                 continue
             name = r["Kernel_Name"]
             key = ("calib" if "bitwise_not" in name else
-                   "split" if f"decode_split_kernel<{group}>" in name else
+                   "split" if f"decode_split_kernel<{group}, false>" in name else
                    "combine" if "decode_combine_kernel" in name else None)
             if key:
                 vals.setdefault(key, []).append(float(r["Counter_Value"]) * 1024.0)
@@ -177,7 +177,8 @@ def small_decode_latency(dev, iters: int, layers: int = 28) -> dict:
     """Time of one small decode step (4 sequences + 2 padding rows, Qwen3-0.6B shape) through
     `layers` attention layers, each with its own pool: store + decode launched eagerly per
     layer vs one HIP-graph replay of all layers (inputs staged into the graph's static buffers
-    once per step). HIP events around each step; median."""
+    once per step), each both as two launches per layer and as the one fused store+decode
+    launch. HIP events around each step; median."""
     from paged_kv_cache_store_amd import graphs
     from paged_kv_cache_store_amd import step as gstep
     from paged_kv_cache_store_amd import workloads
@@ -188,8 +189,11 @@ def small_decode_latency(dev, iters: int, layers: int = 28) -> dict:
     t = ds.tensors
     ks = [kc] + [kc.clone() for _ in range(layers - 1)]
     vs = [vc] + [vc.clone() for _ in range(layers - 1)]
+    assert t.key.shape[0] == t.q_decode.shape[0]  # decode-only step: one new row per sequence
     dg = graphs.DecodeGraphs(w.shape, ks, vs, max_bs=8, max_blocks=ds.decode_tables.shape[1],
                              scale=scale)
+    dgf = graphs.DecodeGraphs(w.shape, ks, vs, max_bs=8, max_blocks=ds.decode_tables.shape[1],
+                              scale=scale, fused=True)
     args = (t.q_decode, t.key, t.value, ds.slot_mapping, ds.context_lens, ds.decode_tables)
 
     def eager():
@@ -197,11 +201,19 @@ def small_decode_latency(dev, iters: int, layers: int = 28) -> dict:
             gstep.run_store(ds, k_l, v_l)
             gstep.run_decode(ds, k_l, v_l, scale)
 
+    def eager_fused():
+        for k_l, v_l in zip(ks, vs):
+            gstep.run_decode_store(ds, k_l, v_l, scale)
+
     def replay():
         dg.run(*args)
 
+    def replay_fused():
+        dgf.run(*args)
+
     res = {"layers": layers}
-    for name, fn in (("eager_us", eager), ("graph_us", replay)):
+    for name, fn in (("eager_us", eager), ("graph_us", replay),
+                     ("eager_fused_us", eager_fused), ("graph_fused_us", replay_fused)):
         for _ in range(5):
             fn()
         torch.cuda.synchronize()
@@ -218,7 +230,7 @@ def small_decode_latency(dev, iters: int, layers: int = 28) -> dict:
         res[name] = round(times[len(times) // 2] * 1e3, 2)  # median, microseconds
     res["rows"] = int(t.q_decode.shape[0])
     res["bucket"] = dg.bucket_for(int(t.q_decode.shape[0]))
-    del dg, ks, vs
+    del dg, dgf, ks, vs
     return res
 
 

@@ -210,6 +210,40 @@ nv_status nv_paged_attn_decode(const void *q, const void *k_cache, const void *v
                                float softmax_scale, void *workspace, size_t workspace_bytes,
                                void *out, hipStream_t stream);
 
+/* ------------------------------------------------------------------------------------------
+ * Store + decode in one launch ("Nano-vLLM Field Guide", Step 10.3: store_kvcache, then
+ * flash_attn_with_kvcache, for a step of decode rows only).
+ *
+ * Same result as nv_store_kvcache(key, key_row_stride, value, value_row_stride, k_cache,
+ * v_cache, slot_mapping, batch, num_kv_heads, head_dim, num_slots) followed by
+ * nv_paged_attn_decode(q, k_cache, v_cache, context_lens, ..., out), bit for bit, provided
+ * that (as for every decode step of the engine) slot_mapping[b] is the pool row of key
+ * context_lens[b] - 1 of row b, and -1 for rows with context_lens[b] == 0, and that no other
+ * row's table reaches that pool row (a shared prefix block is always full, so the block that
+ * takes a new token belongs to one sequence). Row b's new key and value (row b of key / value)
+ * are written to the pools and used directly as key context_lens[b] - 1 of the attention, so
+ * no store kernel runs before it.
+ *
+ *   key, value          device bf16 [batch, num_kv_heads, head_dim] rows with the given row
+ *                       strides (elements), as for nv_store_kvcache; value may be a view into
+ *                       the fused QKV output.
+ *   slot_mapping        device int32 [batch]; -1 stores nothing.
+ *   k_cache, v_cache    the pools, written at the slots and read by the attention.
+ *   num_slots           rows of each pool (host-side argument check only).
+ *   others              as for nv_paged_attn_decode (the same workspace size applies).
+ * With rows that are not 16-byte aligned, or max_blocks_per_seq == 0, the call runs the two
+ * calls above one after the other.
+ * ------------------------------------------------------------------------------------------ */
+nv_status nv_paged_attn_decode_store(const void *q, const void *key, int64_t key_row_stride,
+                                     const void *value, int64_t value_row_stride,
+                                     const int32_t *slot_mapping, void *k_cache, void *v_cache,
+                                     int64_t num_slots, const int32_t *context_lens,
+                                     const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                     int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t block_size, float softmax_scale,
+                                     void *workspace, size_t workspace_bytes, void *out,
+                                     hipStream_t stream);
+
 /* Number of keys one decode work item covers for this launch shape (a multiple of 64): the
  * split the decode call uses. Exposed for tests and measurement. */
 int32_t nv_paged_attn_decode_split_keys(int32_t batch, int32_t num_kv_heads,

@@ -105,6 +105,15 @@ struct DecodeArgs {
     int32_t max_splits;
     float scale_log2;  // softmax_scale * log2(e)
     float rescale_slack;  // raw-score growth of a running max tolerated without a rescale
+    // Fused store (decode rows' new K/V): row b's key and value rows, its slot, and the pools
+    // to write; unused by the plain decode.
+    const uint16_t *new_k;
+    const uint16_t *new_v;
+    int64_t new_k_stride;
+    int64_t new_v_stride;
+    const int32_t *slot_mapping;
+    uint16_t *k_pool;
+    uint16_t *v_pool;
 };
 
 struct Chunk {
@@ -151,7 +160,13 @@ struct DecodeSmem {
 
 // Up to G = 4 the kernel fits 3 waves per SIMD (168 VGPRs) without spilling; the hint makes the
 // compiler hold that budget.
-template <int G>
+//
+// kFused: the call also stores each row's new K/V (the store of this step's decode rows). The
+// workgroup of kv head g that holds a row's last key (key L - 1, the new token) writes head g's
+// key and value rows into the pools at the row's slot and reads that key from the new rows
+// rather than from the pool, so no store kernel has to run first. Rows without keys store from
+// their split-0 workgroups. No other workgroup reads those bytes.
+template <int G, bool kFused>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 : NV_DECODE_MIN_WAVES))) void decode_split_kernel(DecodeArgs a) {
     __shared__ DecodeSmem<G> sm;
 
@@ -162,15 +177,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
 #endif
     const int L = a.context_lens[b];
     const int k0 = s * a.split_keys;
+    // Fused store for a row without keys (no chunk to carry it): head g's 256-byte key and
+    // value rows of row b, 16 lanes x 16 bytes each.
+    auto store_new = [&]() {
+        const int32_t slot = a.slot_mapping[b];
+        if (slot < 0 || threadIdx.x >= 32) return;
+        const int dcs = threadIdx.x & 15;
+        const int64_t dst = ((int64_t)slot * a.num_kv_heads + g) * kHeadDim + 8 * dcs;
+        if (threadIdx.x < 16)
+            *reinterpret_cast<u32x4 *>(a.k_pool + dst) = *reinterpret_cast<const u32x4 *>(
+                a.new_k + (int64_t)b * a.new_k_stride + g * kHeadDim + 8 * dcs);
+        else
+            *reinterpret_cast<u32x4 *>(a.v_pool + dst) = *reinterpret_cast<const u32x4 *>(
+                a.new_v + (int64_t)b * a.new_v_stride + g * kHeadDim + 8 * dcs);
+    };
     if (k0 >= L) {  // past this sequence's context, or a padding row
         if (L <= 0 && s == 0) {  // a row without keys outputs zeros
             for (int idx = threadIdx.x; idx < G * kHeadDim; idx += 256)
                 a.out[((int64_t)b * a.num_heads + g * G) * kHeadDim + idx] = 0;
+            if (kFused) store_new();
         }
         return;
     }
     const int n = min(a.split_keys, L - k0);
     const int nsplit = (L + a.split_keys - 1) / a.split_keys;
+    const bool holds_new = kFused && s == nsplit - 1;  // this split ends with key L - 1
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int bs = a.block_size;
@@ -218,9 +249,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
 #pragma unroll
     for (int i = 0; i < kRowLoads; ++i)
         lane_off[i] = (uint32_t)(((4 * i + sub) * rs + 8 * dc) * 2);
+    // Fused store: the chunk that holds split key n - 1 (the new token) loads that key's
+    // row from the new rows rather than from the pool (an address choice, so the loads stay
+    // in flight like any other). The lanes that loaded it write it to the pools as the chunk
+    // is processed, when its loads are waited for anyway.
+    const uint16_t *new_k_row = kFused ? a.new_k + (int64_t)b * a.new_k_stride + g * kHeadDim
+                                       : nullptr;
+    const uint16_t *new_v_row = kFused ? a.new_v + (int64_t)b * a.new_v_stride + g * kHeadDim
+                                       : nullptr;
+    auto put_new = [&](const Chunk &buf, int kc) {
+        const int r = n - 1 - kc;
+        if (r >= kChunk || sub != (r & 3)) return;
+        const int32_t slot = a.slot_mapping[b];
+        if (slot < 0) return;
+        const int64_t dst = ((int64_t)slot * a.num_kv_heads + g) * kHeadDim + 8 * dc;
+        // Register selects (a store per candidate row would be merged into one store indexed
+        // at run time, which puts the chunk in scratch memory).
+        u32x4 kn = buf.k[0], vn = buf.v[0];
+#pragma unroll
+        for (int i = 1; i < kRowLoads; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                kn[e] = i == (r >> 2) ? buf.k[i][e] : kn[e];
+                vn[e] = i == (r >> 2) ? buf.v[i][e] : vn[e];
+            }
+        *reinterpret_cast<u32x4 *>(a.k_pool + dst) = kn;
+        *reinterpret_cast<u32x4 *>(a.v_pool + dst) = vn;
+    };
     auto load_chunk = [&](Chunk &buf, int ch) {
         const int kc = ch * kChunk;
-        if (chunk_in_block && kc + kChunk <= n) {
+        const bool tail_new = holds_new && n - kc <= kChunk;  // wave-uniform
+        if (chunk_in_block && kc + kChunk <= n && !tail_new) {
             const int j = k0 + kc;
             int lb, off;
             if (a.bs_shift >= 0) {
@@ -246,9 +305,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
             const int jl = kc + 4 * i + sub;
             const bool ok = jl < n;
             const int64_t off = (ok ? row_of(jl) : 0) * rs + 8 * dc;
-            buf.k[i] = ok ? NV_LOAD_STREAM(reinterpret_cast<const u32x4 *>(kbase + off))
+            const uint16_t *kr = kbase + off, *vr = vbase + off;
+            if (kFused && tail_new && jl == n - 1) {
+                // Formed here, not hoisted: two more 64-bit addresses live through the loop
+                // would spill at G = 4.
+                uint32_t lo = 16 * dc;
+                asm volatile("" : "+v"(lo));
+                kr = reinterpret_cast<const uint16_t *>(
+                    reinterpret_cast<const char *>(new_k_row) + lo);
+                vr = reinterpret_cast<const uint16_t *>(
+                    reinterpret_cast<const char *>(new_v_row) + lo);
+            }
+            buf.k[i] = ok ? NV_LOAD_STREAM(reinterpret_cast<const u32x4 *>(kr))
                           : u32x4{0, 0, 0, 0};
-            buf.v[i] = ok ? NV_LOAD_STREAM(reinterpret_cast<const u32x4 *>(vbase + off))
+            buf.v[i] = ok ? NV_LOAD_STREAM(reinterpret_cast<const u32x4 *>(vr))
                           : u32x4{0, 0, 0, 0};
         }
     };
@@ -427,10 +497,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
     if (ch < nch) load_chunk(A, ch);
     while (ch < nch) {
         if (ch + 4 < nch) load_chunk(B, ch + 4);
+        if (holds_new) put_new(A, ch * kChunk);
         process(A, ch);
         ch += 4;
         if (ch >= nch) break;
         if (ch + 4 < nch) load_chunk(A, ch + 4);
+        if (holds_new) put_new(B, ch * kChunk);
         process(B, ch);
         ch += 4;
     }
@@ -511,14 +583,14 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
     a.out[bh * kHeadDim + e] = __builtin_bit_cast(uint16_t, (__bf16)(num / den));
 }
 
-template <int G>
+template <int G, bool kFused>
 nv_status launch_decode(const DecodeArgs &a, int batch, hipStream_t stream) {
 #if NV_DECODE_HEAD_MAJOR
     const dim3 grid(a.num_kv_heads, a.max_splits, batch);
 #else
     const dim3 grid(a.max_splits, a.num_kv_heads, batch);
 #endif
-    nv_status st = launch(decode_split_kernel<G>, grid, dim3(256), 0, stream, a);
+    nv_status st = launch(decode_split_kernel<G, kFused>, grid, dim3(256), 0, stream, a);
     if (st != NV_OK || a.max_splits == 1) return st;  // one split: every row is final already
     return launch(decode_combine_kernel, dim3(a.num_heads, batch), dim3(kHeadDim), 0, stream, a);
 }
@@ -562,6 +634,28 @@ extern "C" size_t nv_paged_attn_decode_workspace_size(int32_t batch, int32_t num
     return ml + rows * head_dim * sizeof(float);
 }
 
+namespace nvp {
+namespace {
+
+// The decode rows' new K/V for the fused call (null for the plain decode).
+struct FusedStore {
+    const uint16_t *key;
+    int64_t key_row_stride;
+    const uint16_t *value;
+    int64_t value_row_stride;
+    const int32_t *slot_mapping;
+};
+
+nv_status decode_impl(const void *q, const void *k_cache, const void *v_cache,
+                      const int32_t *context_lens, const int32_t *block_tables,
+                      int32_t max_blocks_per_seq, int32_t batch, int32_t num_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                      float softmax_scale, void *workspace, size_t workspace_bytes, void *out,
+                      hipStream_t stream, const FusedStore *fs);
+
+}  // namespace
+}  // namespace nvp
+
 extern "C" nv_status nv_paged_attn_decode(const void *q, const void *k_cache,
                                           const void *v_cache, const int32_t *context_lens,
                                           const int32_t *block_tables,
@@ -571,7 +665,56 @@ extern "C" nv_status nv_paged_attn_decode(const void *q, const void *k_cache,
                                           float softmax_scale, void *workspace,
                                           size_t workspace_bytes, void *out,
                                           hipStream_t stream) {
+    return nvp::decode_impl(q, k_cache, v_cache, context_lens, block_tables, max_blocks_per_seq,
+                            batch, num_heads, num_kv_heads, head_dim, block_size, softmax_scale,
+                            workspace, workspace_bytes, out, stream, nullptr);
+}
+
+extern "C" nv_status nv_paged_attn_decode_store(
+    const void *q, const void *key, int64_t key_row_stride, const void *value,
+    int64_t value_row_stride, const int32_t *slot_mapping, void *k_cache, void *v_cache,
+    int64_t num_slots, const int32_t *context_lens, const int32_t *block_tables,
+    int32_t max_blocks_per_seq, int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, float softmax_scale, void *workspace,
+    size_t workspace_bytes, void *out, hipStream_t stream) {
     using namespace nvp;
+    if (batch < 0 || num_kv_heads <= 0 || head_dim <= 0 || num_slots < 0)
+        return NV_ERR_INVALID_ARG;
+    const int64_t D = (int64_t)num_kv_heads * head_dim;
+    if (key_row_stride < D || value_row_stride < D) return NV_ERR_INVALID_ARG;
+    if (batch > 0 && (!key || !value || !slot_mapping || !k_cache || !v_cache))
+        return NV_ERR_INVALID_ARG;
+    // One launch needs whole 16-byte lanes; otherwise (or with no key slots at all) the store
+    // and the decode run one after the other, with the same result.
+    const auto a16 = [](const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+    const bool fusable = key_row_stride % 8 == 0 && value_row_stride % 8 == 0 && a16(key) &&
+                         a16(value) && a16(k_cache) && a16(v_cache) && max_blocks_per_seq > 0;
+    if (!fusable) {
+        const nv_status st = nv_store_kvcache(key, key_row_stride, value, value_row_stride,
+                                              k_cache, v_cache, slot_mapping, batch,
+                                              num_kv_heads, head_dim, num_slots, stream);
+        if (st != NV_OK) return st;
+        return nv_paged_attn_decode(q, k_cache, v_cache, context_lens, block_tables,
+                                    max_blocks_per_seq, batch, num_heads, num_kv_heads, head_dim,
+                                    block_size, softmax_scale, workspace, workspace_bytes, out,
+                                    stream);
+    }
+    const FusedStore fs{static_cast<const uint16_t *>(key), key_row_stride,
+                        static_cast<const uint16_t *>(value), value_row_stride, slot_mapping};
+    return decode_impl(q, k_cache, v_cache, context_lens, block_tables, max_blocks_per_seq, batch,
+                       num_heads, num_kv_heads, head_dim, block_size, softmax_scale, workspace,
+                       workspace_bytes, out, stream, &fs);
+}
+
+namespace nvp {
+namespace {
+
+nv_status decode_impl(const void *q, const void *k_cache, const void *v_cache,
+                      const int32_t *context_lens, const int32_t *block_tables,
+                      int32_t max_blocks_per_seq, int32_t batch, int32_t num_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                      float softmax_scale, void *workspace, size_t workspace_bytes, void *out,
+                      hipStream_t stream, const FusedStore *fs) {
     if (batch < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
         max_blocks_per_seq < 0)
         return NV_ERR_INVALID_ARG;
@@ -625,14 +768,36 @@ extern "C" nv_status nv_paged_attn_decode(const void *q, const void *k_cache,
                   : nullptr;
     a.scale_log2 = softmax_scale * kLog2e;
     a.rescale_slack = NV_DECODE_SLACK / a.scale_log2;
+    a.new_k = fs ? fs->key : nullptr;
+    a.new_v = fs ? fs->value : nullptr;
+    a.new_k_stride = fs ? fs->key_row_stride : 0;
+    a.new_v_stride = fs ? fs->value_row_stride : 0;
+    a.slot_mapping = fs ? fs->slot_mapping : nullptr;
+    a.k_pool = fs ? static_cast<uint16_t *>(const_cast<void *>(k_cache)) : nullptr;
+    a.v_pool = fs ? static_cast<uint16_t *>(const_cast<void *>(v_cache)) : nullptr;
+    if (fs) {
+        switch (G) {
+            case 1: return launch_decode<1, true>(a, batch, stream);
+            case 2: return launch_decode<2, true>(a, batch, stream);
+            case 3: return launch_decode<3, true>(a, batch, stream);
+            case 4: return launch_decode<4, true>(a, batch, stream);
+            case 5: return launch_decode<5, true>(a, batch, stream);
+            case 6: return launch_decode<6, true>(a, batch, stream);
+            case 7: return launch_decode<7, true>(a, batch, stream);
+            default: return launch_decode<8, true>(a, batch, stream);
+        }
+    }
     switch (G) {
-        case 1: return launch_decode<1>(a, batch, stream);
-        case 2: return launch_decode<2>(a, batch, stream);
-        case 3: return launch_decode<3>(a, batch, stream);
-        case 4: return launch_decode<4>(a, batch, stream);
-        case 5: return launch_decode<5>(a, batch, stream);
-        case 6: return launch_decode<6>(a, batch, stream);
-        case 7: return launch_decode<7>(a, batch, stream);
-        default: return launch_decode<8>(a, batch, stream);
+        case 1: return launch_decode<1, false>(a, batch, stream);
+        case 2: return launch_decode<2, false>(a, batch, stream);
+        case 3: return launch_decode<3, false>(a, batch, stream);
+        case 4: return launch_decode<4, false>(a, batch, stream);
+        case 5: return launch_decode<5, false>(a, batch, stream);
+        case 6: return launch_decode<6, false>(a, batch, stream);
+        case 7: return launch_decode<7, false>(a, batch, stream);
+        default: return launch_decode<8, false>(a, batch, stream);
     }
 }
+
+}  // namespace
+}  // namespace nvp

@@ -11,7 +11,8 @@ pool or the real rows. Block-table rows are not cleared between steps: entries p
 own context are never read.
 
 The recorded launches are the library's kernels only (no memset nodes); padding values are
-written by ordinary eager fills before the replay.
+written by ordinary eager fills before the replay. With ``fused=True`` each layer records one
+store+decode call (nv_paged_attn_decode_store) instead of the store and the decode.
 """
 from __future__ import annotations
 
@@ -37,10 +38,11 @@ class DecodeGraphs:
     the block size)."""
 
     def __init__(self, shape: AttnShape, k_cache, v_cache, max_bs: int, max_blocks: int,
-                 scale: float | None = None):
+                 scale: float | None = None, fused: bool = False):
         if max_bs < 1 or max_blocks < 1:
             raise ValueError("max_bs and max_blocks must be positive")
         self.shape = shape
+        self.fused = fused  # one store+decode launch per layer instead of two
         self.k_caches = list(k_cache) if isinstance(k_cache, (list, tuple)) else [k_cache]
         self.v_caches = list(v_cache) if isinstance(v_cache, (list, tuple)) else [v_cache]
         if len(self.k_caches) != len(self.v_caches) or not self.k_caches:
@@ -79,6 +81,13 @@ class DecodeGraphs:
     def _launch(self, bs: int) -> None:
         s = self.shape
         for layer, (kc, vc) in enumerate(zip(self.k_caches, self.v_caches)):
+            if self.fused:
+                nvpaged.nv_paged_attn_decode_store(
+                    self.q[:bs], self.key[:bs], self.value[:bs], self.slot_mapping[:bs], kc, vc,
+                    self.context_lens[:bs], self.block_tables[:bs], s.num_kv_heads,
+                    s.block_size, self.scale, workspace=self.workspace,
+                    out=self.out[layer, :bs])
+                continue
             nvpaged.nv_store_kvcache(self.key[:bs], self.value[:bs], kc, vc,
                                      self.slot_mapping[:bs])
             nvpaged.nv_paged_attn_decode(self.q[:bs], kc, vc, self.context_lens[:bs],

@@ -23,7 +23,8 @@ if not os.path.exists(LIB_PATH):
 EXPORTS = ("nv_status_string", "nv_store_kvcache", "nv_paged_attn_prefill",
            "nv_attn_prefill_packed", "nv_qk_norm_rope_store",
            "nv_paged_attn_decode_workspace_size", "nv_paged_attn_decode",
-           "nv_paged_attn_decode_split_keys", "nv_prepare_prefill", "nv_prepare_decode",
+           "nv_paged_attn_decode_split_keys", "nv_paged_attn_decode_store",
+           "nv_prepare_prefill", "nv_prepare_decode",
            "nv_check_indices")
 
 _p, _i32, _i64, _f32, _sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
@@ -53,6 +54,10 @@ def _bind(path: str) -> ctypes.CDLL:
     L.nv_paged_attn_decode.argtypes = [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
                                        _f32, _p, _sz, _p, _p]
     L.nv_paged_attn_decode.restype = ctypes.c_int
+    L.nv_paged_attn_decode_store.argtypes = [_p, _p, _i64, _p, _i64, _p, _p, _p, _i64, _p, _p,
+                                             _i32, _i32, _i32, _i32, _i32, _i32, _f32, _p, _sz,
+                                             _p, _p]
+    L.nv_paged_attn_decode_store.restype = ctypes.c_int
     L.nv_prepare_prefill.argtypes = [_p, _p, _p, _p, _i32, _i32, _p, _p, _p, _p, _p, _p, _i32,
                                      _p]
     L.nv_prepare_prefill.restype = ctypes.c_int
@@ -320,6 +325,52 @@ def nv_paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
                                      int(block_size), float(softmax_scale), workspace.data_ptr(),
                                      workspace.numel() * workspace.element_size(), out.data_ptr(),
                                      _stream(stream)), "nv_paged_attn_decode")
+    return out
+
+
+def nv_paged_attn_decode_store(q: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                               slot_mapping: torch.Tensor, k_cache: torch.Tensor,
+                               v_cache: torch.Tensor, context_lens: torch.Tensor,
+                               block_tables: torch.Tensor, num_kv_heads: int, block_size: int,
+                               softmax_scale: float, workspace: torch.Tensor | None = None,
+                               out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Store of the decode rows' key/value [B, Hkv, d] at slot_mapping [B], then decode
+    attention of q [B, Hq, d], in one launch; returns out [B, Hq, d] bf16."""
+    _dev(q, "q", torch.bfloat16)
+    if q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [batch, num_heads, head_dim] tensor")
+    b, hq, d = q.shape
+    for t, nm in ((key, "key"), (value, "value")):
+        _dev(t, nm, torch.bfloat16)
+        if t.dim() != 3 or t.shape != (b, num_kv_heads, d) or t.stride(2) != 1 or t.stride(1) != d:
+            raise ValueError(f"{nm} must be [batch, num_kv_heads, head_dim] with contiguous heads")
+    _dev(slot_mapping, "slot_mapping", torch.int32)
+    if slot_mapping.numel() != b or not slot_mapping.is_contiguous():
+        raise ValueError("slot_mapping must be contiguous with one entry per row")
+    ns = _pool_rows(k_cache, "k_cache", num_kv_heads * d)
+    if _pool_rows(v_cache, "v_cache", num_kv_heads * d) != ns:
+        raise ValueError("k_cache and v_cache differ in size")
+    _dev(context_lens, "context_lens", torch.int32)
+    _dev(block_tables, "block_tables", torch.int32)
+    if context_lens.numel() != b or not context_lens.is_contiguous():
+        raise ValueError("context_lens must have one entry per row")
+    if block_tables.dim() != 2 or block_tables.shape[0] != b or not block_tables.is_contiguous():
+        raise ValueError("block_tables must be a contiguous [batch, max_blocks] tensor")
+    if workspace is None:
+        workspace = decode_workspace(q, num_kv_heads, block_tables, block_size)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _dev(out, "out", torch.bfloat16)
+        if out.shape != q.shape or not out.is_contiguous():
+            raise ValueError("out must be contiguous and shaped like q")
+    _check(_lib.nv_paged_attn_decode_store(
+        q.data_ptr(), key.data_ptr(), key.stride(0), value.data_ptr(), value.stride(0),
+        slot_mapping.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), ns,
+        context_lens.data_ptr(), block_tables.data_ptr(), block_tables.shape[1], b, hq,
+        int(num_kv_heads), d, int(block_size), float(softmax_scale), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), out.data_ptr(), _stream(stream)),
+        "nv_paged_attn_decode_store")
     return out
 
 

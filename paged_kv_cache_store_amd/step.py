@@ -132,6 +132,20 @@ def run_decode(ds: DeviceStep, k_cache, v_cache, scale: float, stream=None) -> N
                                  workspace=ds.workspace, out=ds.out_decode, stream=stream)
 
 
+def run_decode_store(ds: DeviceStep, k_cache, v_cache, scale: float, stream=None) -> None:
+    """A decode-only step's store and decode in one launch (the step's rows are all decode
+    rows, one per sequence, in the order of ``context_lens``)."""
+    if ds.context_lens is None:
+        return
+    s = ds.shape
+    t = ds.tensors
+    nvpaged.nv_paged_attn_decode_store(t.q_decode, t.key, t.value, ds.slot_mapping, k_cache,
+                                       v_cache, ds.context_lens, ds.decode_tables,
+                                       s.num_kv_heads, s.block_size, scale,
+                                       workspace=ds.workspace, out=ds.out_decode,
+                                       stream=stream)
+
+
 def run_step(ds: DeviceStep, k_cache, v_cache, scale: Optional[float] = None, stream=None):
     """store -> prefill -> decode on one stream; returns (prefill_out, decode_out)."""
     if scale is None:

@@ -166,6 +166,30 @@ def test_device_calls_reject_bad_arguments_without_launch(nv):
                                   null) == 0  # empty batch
 
 
+def test_decode_store_argument_errors(nv):
+    """The one-launch store + decode rejects bad store arguments before launching anything."""
+    L = nv.lib()
+    null = None
+    # key null, key row stride below Hkv * d, negative num_slots, null slot_mapping
+    assert L.nv_paged_attn_decode_store(1, null, 1024, 1, 1024, 1, 1, 1, 100, 1, 1, 3, 4, 16, 8,
+                                        128, 256, 0.1, 256, 1 << 20, 1, null) == -1
+    assert L.nv_paged_attn_decode_store(1, 1, 512, 1, 1024, 1, 1, 1, 100, 1, 1, 3, 4, 16, 8,
+                                        128, 256, 0.1, 256, 1 << 20, 1, null) == -1
+    assert L.nv_paged_attn_decode_store(1, 1, 1024, 1, 1024, 1, 1, 1, -1, 1, 1, 3, 4, 16, 8,
+                                        128, 256, 0.1, 256, 1 << 20, 1, null) == -1
+    assert L.nv_paged_attn_decode_store(1, 16, 1024, 16, 1024, null, 16, 16, 100, 1, 1, 3, 4,
+                                        16, 8, 128, 256, 0.1, 256, 1 << 20, 1, null) == -1
+    # decode-side errors surface unchanged (16-byte aligned dummies: the fused path is taken)
+    assert L.nv_paged_attn_decode_store(16, 16, 1024, 16, 1024, 16, 16, 16, 100, 16, 16, 3, 4,
+                                        16, 8, 128, 256, 0.0, 256, 1 << 20, 16, null) == -1
+    assert L.nv_paged_attn_decode_store(16, 16, 1024, 16, 1024, 16, 16, 16, 100, 16, 16, 3, 4,
+                                        16, 8, 64, 256, 0.1, 256, 1 << 20, 16, null) == -2
+    # empty batch: nothing to do
+    assert L.nv_paged_attn_decode_store(null, null, 1024, null, 1024, null, null, null, 0, null,
+                                        null, 3, 0, 16, 8, 128, 256, 0.1, null, 0, null,
+                                        null) == 0
+
+
 def test_decode_split_choice(nv):
     # Small batches get short splits so the chip fills; large ones get long splits (few
     # partial results): 2048 (sequence, kv head) pairs or more run unsplit up to 8192 keys.

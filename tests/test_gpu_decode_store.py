@@ -1,0 +1,105 @@
+"""GPU parity of the one-launch store + decode (nv_paged_attn_decode_store).
+
+It must equal nv_store_kvcache followed by nv_paged_attn_decode bit for bit (pools and
+outputs), for split and unsplit launches, padding rows and several shapes and block sizes;
+and, on its own, match the oracle's store (bit-exact pools) and decode (attention bound).
+"""
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_store_amd import graphs, nvpaged, workloads
+from paged_kv_cache_store_amd import step as gstep
+from gpu_common import Run, assert_attn_close, check_pools_bit_exact
+from helpers import bits
+
+pytestmark = pytest.mark.gpu
+
+CASES = [  # shape, decode rows, max context, padding rows
+    (workloads.QWEN3_0_6B, 4, 600, 2),        # small batch: 128-key splits, merge kernel
+    (workloads.QWEN3_8B, 9, 3000, 1),
+    (workloads.AttnShape(12, 4, 128, 16), 7, 900, 2),
+    (workloads.AttnShape(32, 4, 128, 48), 5, 700, 0),
+    (workloads.AttnShape(16, 8, 128, 256), 300, 1500, 4),  # 2400 pairs: unsplit, no merge
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[0].num_heads}q{c[0].num_kv_heads}kv_bs{c[0].block_size}_B{c[1]}")
+def test_fused_equals_store_then_decode(case):
+    shape, n, max_len, pad = case
+    w = workloads.random_workload(60 + n, shape, 0, n, max_len=max_len, pad_rows=pad)
+    print(f"[decode_store] {shape} rows={n}+{pad}", flush=True)
+    run_a = Run(w)
+    run_b = Run(w)
+    scale = run_a.scale
+    ds_a = gstep.prepare_step(shape, w.steps[0], run_a.tensors[0], "cuda")
+    ds_b = gstep.prepare_step(shape, w.steps[0], run_b.tensors[0], "cuda")
+    # reference composition
+    gstep.run_store(ds_a, run_a.k_cache, run_a.v_cache)
+    gstep.run_decode(ds_a, run_a.k_cache, run_a.v_cache, scale)
+    # fused, into an output that starts as NaN
+    t = ds_b.tensors
+    out = torch.full_like(t.q_decode, float("nan"))
+    nvpaged.nv_paged_attn_decode_store(t.q_decode, t.key, t.value, ds_b.slot_mapping,
+                                       run_b.k_cache, run_b.v_cache, ds_b.context_lens,
+                                       ds_b.decode_tables, shape.num_kv_heads, shape.block_size,
+                                       scale, out=out)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(run_a.k_cache), bits(run_b.k_cache))
+    assert np.array_equal(bits(run_a.v_cache), bits(run_b.v_cache))
+    assert np.array_equal(bits(ds_a.out_decode), bits(out)), "outputs differ"
+    # and against the oracle
+    run_b.oracle_store(0)
+    check_pools_bit_exact(run_b, "fused store")
+    ids, ref = run_b.oracle_decode(0)
+    print(assert_attn_close(out[ids], ref, "fused decode"))
+
+
+def test_fused_unaligned_rows_fall_back():
+    """A value view whose rows are not 16-byte aligned takes the two-call path, same result."""
+    shape = workloads.AttnShape(8, 2, 128, 64)
+    w = workloads.random_workload(71, shape, 0, 5, max_len=300, pad_rows=1)
+    run_a, run_b = Run(w), Run(w)
+    ds_a = gstep.prepare_step(shape, w.steps[0], run_a.tensors[0], "cuda")
+    ds_b = gstep.prepare_step(shape, w.steps[0], run_b.tensors[0], "cuda")
+    gstep.run_store(ds_a, run_a.k_cache, run_a.v_cache)
+    gstep.run_decode(ds_a, run_a.k_cache, run_a.v_cache, run_a.scale)
+    t = ds_b.tensors
+    # copy the value rows into a buffer offset by one element: row pointers lose 16-B alignment
+    n = t.value.shape[0]
+    raw = torch.empty(n * 264 + 8, dtype=torch.bfloat16, device="cuda")
+    val = raw[1:1 + n * 264].view(n, 264)[:, :256].view(n, 2, 128)
+    val.copy_(t.value)
+    assert val.data_ptr() % 16 != 0
+    out = nvpaged.nv_paged_attn_decode_store(t.q_decode, t.key, val, ds_b.slot_mapping,
+                                             run_b.k_cache, run_b.v_cache, ds_b.context_lens,
+                                             ds_b.decode_tables, 2, 64, run_b.scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(run_a.v_cache), bits(run_b.v_cache))
+    assert np.array_equal(bits(ds_a.out_decode), bits(out))
+
+
+def test_fused_graph_replay_matches_two_call_graph():
+    """Decode graphs recorded with the fused call replay to the same outputs and pools as the
+    two-call graphs, over several steps of a small batch."""
+    shape = workloads.QWEN3_0_6B
+    w = workloads.config_decode_small()
+    res = []
+    for fused in (False, True):
+        run = Run(w)
+        ds = gstep.prepare_step(shape, w.steps[0], run.tensors[0], "cuda")
+        dg = graphs.DecodeGraphs(shape, run.k_cache, run.v_cache, max_bs=8,
+                                 max_blocks=ds.decode_tables.shape[1], scale=run.scale,
+                                 fused=fused)
+        t = ds.tensors
+        outs = []
+        for _ in range(3):
+            o = dg.run(t.q_decode, t.key, t.value, ds.slot_mapping, ds.context_lens,
+                       ds.decode_tables)
+            torch.cuda.synchronize()
+            outs.append(bits(o).copy())
+        res.append((outs, bits(run.k_cache).copy(), bits(run.v_cache).copy()))
+    (o0, k0, v0), (o1, k1, v1) = res
+    for a, b in zip(o0, o1):
+        assert np.array_equal(a, b)
+    assert np.array_equal(k0, k1) and np.array_equal(v0, v1)

@@ -230,9 +230,20 @@ nv_status nv_paged_attn_decode(const void *q, const void *k_cache, const void *v
  *   slot_mapping        device int32 [batch]; -1 stores nothing.
  *   k_cache, v_cache    the pools, written at the slots and read by the attention.
  *   num_slots           rows of each pool (host-side argument check only).
+ *   counters            optional device uint32 [num_counters], num_counters >= batch *
+ *                       num_kv_heads, entry b * num_kv_heads + g for row b, kv head g. Given,
+ *                       the split kernel also merges the splits of a split row (the last of
+ *                       its workgroups to finish merges), so no merge kernel runs and the call
+ *                       is one launch. The entries must be zero before the call, and the call
+ *                       leaves them zero; the layout does not depend on anything but batch
+ *                       and num_kv_heads, so one zeroed array serves calls of any batch up to
+ *                       its size (and is untouched by calls that do not split). Calls that run
+ *                       concurrently need separate arrays. NULL: the merge kernel runs.
  *   others              as for nv_paged_attn_decode (the same workspace size applies).
- * With rows that are not 16-byte aligned, or max_blocks_per_seq == 0, the call runs the two
- * calls above one after the other.
+ * The output is the same bit for bit with or without counters. With rows that are not 16-byte
+ * aligned, or max_blocks_per_seq == 0, the call runs the two calls above one after the other
+ * (counters untouched). Errors: as the two calls, and NV_ERR_INVALID_ARG for counters that
+ * are too short or not 4-byte aligned.
  * ------------------------------------------------------------------------------------------ */
 nv_status nv_paged_attn_decode_store(const void *q, const void *key, int64_t key_row_stride,
                                      const void *value, int64_t value_row_stride,
@@ -241,7 +252,8 @@ nv_status nv_paged_attn_decode_store(const void *q, const void *key, int64_t key
                                      const int32_t *block_tables, int32_t max_blocks_per_seq,
                                      int32_t batch, int32_t num_heads, int32_t num_kv_heads,
                                      int32_t head_dim, int32_t block_size, float softmax_scale,
-                                     void *workspace, size_t workspace_bytes, void *out,
+                                     void *workspace, size_t workspace_bytes,
+                                     uint32_t *counters, int64_t num_counters, void *out,
                                      hipStream_t stream);
 
 /* Number of keys one decode work item covers for this launch shape (a multiple of 64): the

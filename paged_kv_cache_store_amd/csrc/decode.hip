@@ -11,7 +11,7 @@
 //  - Work item = (sequence b, kv head g, split s of the key range). The G query heads of the
 //    group share every K/V load. The split's slice of the block table is staged in LDS once,
 //    so no K/V address waits on a table load.
-//  - Each of the 4 waves of a workgroup walks its own chunks of 32 keys (chunks w, w+4, ...)
+//  - Each of the 4 waves of a workgroup walks its own chunks of 16 keys (chunks w, w+4, ...)
 //    with an online softmax. K and V of the next chunk are loaded while the current one is
 //    processed (two register buffers), 16 KiB per wave in flight.
 //  - Lane layout: 16 lanes x 16 B cover one 256-byte key (or value) row of the kv head, a wave
@@ -41,6 +41,11 @@
 //  - Grid order: the kv heads of one (sequence, split) are consecutive workgroups, so the
 //    G-head slices of the same pool rows are read at the same time (measured +9% on the
 //    Qwen3-8B decode over split-major order).
+//  - One-launch store + decode (nv_paged_attn_decode_store, a decode step's two calls): the
+//    workgroup holding a row's new token loads that key's row from the step's new K/V rows and
+//    writes it to the pools; with arrival counters the last workgroup of a split row to finish
+//    merges the partials itself (coherent relaxed-atomic partials, no cache-wide fence), so
+//    neither a store kernel nor a merge kernel runs.
 // The split size depends only on host-known launch parameters: no device round trip.
 #include "nv_common.h"
 
@@ -114,6 +119,9 @@ struct DecodeArgs {
     const int32_t *slot_mapping;
     uint16_t *k_pool;
     uint16_t *v_pool;
+    // Arrival counters of the in-kernel merge, [B * Hkv] (null: the merge kernel runs). Zero
+    // before the launch; the workgroup that merges a row returns its counter to zero.
+    uint32_t *counters;
 };
 
 struct Chunk {
@@ -156,7 +164,39 @@ struct DecodeSmem {
     int32_t table[kTableSlots];
     float o[4][G][kHeadDim];
     float ml[4][G][2];
+    int32_t merges;  // in-kernel merge: this workgroup arrived last for its row
 };
+
+// Partials of the in-kernel merge are written and read as relaxed agent-scope atomics: on
+// gfx950 those bypass the caches that are not coherent across XCDs (sc1), so they need no
+// cache-wide write-back or invalidate, which a device-scope fence would do in every workgroup.
+template <bool kCoherent>
+__device__ __forceinline__ float ld_part(const float *p) {
+    if constexpr (kCoherent) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else return *p;
+}
+template <bool kCoherent>
+__device__ __forceinline__ void st_part(float *p, float v) {
+    if constexpr (kCoherent) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else *p = v;
+}
+
+// Log-sum-exp merge of the nsplit partials of row bh at dim e, in split order; the merge
+// kernel and the in-kernel merge share it, so both give the same bits.
+template <bool kCoherent = false>
+__device__ __forceinline__ float merge_splits(const DecodeArgs &a, int64_t bh, int nsplit,
+                                              int e) {
+    const float *ml = a.ws_ml + bh * a.max_splits * 2;
+    float M = -INFINITY;
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ld_part<kCoherent>(ml + 2 * s));
+    float num = 0.f, den = 0.f;
+    for (int s = 0; s < nsplit; ++s) {
+        const float w = fast_exp2(ld_part<kCoherent>(ml + 2 * s) - M);
+        den = fmaf(w, ld_part<kCoherent>(ml + 2 * s + 1), den);
+        num = fmaf(w, ld_part<kCoherent>(a.ws_o + (bh * a.max_splits + s) * kHeadDim + e), num);
+    }
+    return num / den;
+}
 
 // Up to G = 4 the kernel fits 3 waves per SIMD (168 VGPRs) without spilling; the hint makes the
 // compiler hold that budget.
@@ -550,6 +590,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
         const int64_t bh = (int64_t)b * a.num_heads + g * G + h;
         if (nsplit == 1) {
             a.out[bh * kHeadDim + e] = __builtin_bit_cast(uint16_t, (__bf16)(num / den));
+        } else if (kFused && a.counters) {
+            st_part<true>(a.ws_o + (bh * a.max_splits + s) * kHeadDim + e, num);
+            if (e == 0) {
+                st_part<true>(a.ws_ml + (bh * a.max_splits + s) * 2, M);
+                st_part<true>(a.ws_ml + (bh * a.max_splits + s) * 2 + 1, den);
+            }
         } else {
             a.ws_o[(bh * a.max_splits + s) * kHeadDim + e] = num;
             if (e == 0) {
@@ -557,6 +603,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
                 a.ws_ml[(bh * a.max_splits + s) * 2 + 1] = den;
             }
         }
+    }
+    if (!kFused || nsplit == 1 || a.counters == nullptr) return;
+
+    // In-kernel merge: the last of the row's nsplit workgroups to finish merges all partials.
+    // Every wave waits until its (coherent) partial stores have completed, the workgroup
+    // meets, and one lane counts the arrival; the workgroup that brings the count to nsplit
+    // reads the partials with coherent loads, issued only after the count returned. Nothing
+    // waits on another workgroup, so any dispatch order completes.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    uint32_t *cnt = a.counters + (int64_t)b * a.num_kv_heads + g;
+    if (tid == 0)
+        sm.merges = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                    (uint32_t)(nsplit - 1);
+    __syncthreads();
+    if (!sm.merges) return;
+    if (tid == 0)  // ready for the next call
+        __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int idx = tid; idx < G * kHeadDim; idx += 256) {
+        const int h = idx / kHeadDim, e = idx % kHeadDim;
+        const int64_t bh = (int64_t)b * a.num_heads + g * G + h;
+        a.out[bh * kHeadDim + e] =
+            __builtin_bit_cast(uint16_t, (__bf16)merge_splits<true>(a, bh, nsplit, e));
     }
 }
 
@@ -571,16 +640,7 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
     }
     const int nsplit = (L + a.split_keys - 1) / a.split_keys;
     if (nsplit == 1) return;  // the split kernel wrote the final row
-    const float *ml = a.ws_ml + bh * a.max_splits * 2;
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ml[2 * s]);
-    float num = 0.f, den = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-        const float w = fast_exp2(ml[2 * s] - M);
-        den = fmaf(w, ml[2 * s + 1], den);
-        num = fmaf(w, a.ws_o[(bh * a.max_splits + s) * kHeadDim + e], num);
-    }
-    a.out[bh * kHeadDim + e] = __builtin_bit_cast(uint16_t, (__bf16)(num / den));
+    a.out[bh * kHeadDim + e] = __builtin_bit_cast(uint16_t, (__bf16)merge_splits(a, bh, nsplit, e));
 }
 
 template <int G, bool kFused>
@@ -591,7 +651,8 @@ nv_status launch_decode(const DecodeArgs &a, int batch, hipStream_t stream) {
     const dim3 grid(a.max_splits, a.num_kv_heads, batch);
 #endif
     nv_status st = launch(decode_split_kernel<G, kFused>, grid, dim3(256), 0, stream, a);
-    if (st != NV_OK || a.max_splits == 1) return st;  // one split: every row is final already
+    // One split: every row is final already. With counters the split kernel merged.
+    if (st != NV_OK || a.max_splits == 1 || (kFused && a.counters)) return st;
     return launch(decode_combine_kernel, dim3(a.num_heads, batch), dim3(kHeadDim), 0, stream, a);
 }
 
@@ -644,6 +705,7 @@ struct FusedStore {
     const uint16_t *value;
     int64_t value_row_stride;
     const int32_t *slot_mapping;
+    uint32_t *counters;  // in-kernel merge counters [B * Hkv], or null
 };
 
 nv_status decode_impl(const void *q, const void *k_cache, const void *v_cache,
@@ -676,9 +738,13 @@ extern "C" nv_status nv_paged_attn_decode_store(
     int64_t num_slots, const int32_t *context_lens, const int32_t *block_tables,
     int32_t max_blocks_per_seq, int32_t batch, int32_t num_heads, int32_t num_kv_heads,
     int32_t head_dim, int32_t block_size, float softmax_scale, void *workspace,
-    size_t workspace_bytes, void *out, hipStream_t stream) {
+    size_t workspace_bytes, uint32_t *counters, int64_t num_counters, void *out,
+    hipStream_t stream) {
     using namespace nvp;
     if (batch < 0 || num_kv_heads <= 0 || head_dim <= 0 || num_slots < 0)
+        return NV_ERR_INVALID_ARG;
+    if (counters && (num_counters < (int64_t)batch * num_kv_heads ||
+                     reinterpret_cast<uintptr_t>(counters) % 4 != 0))
         return NV_ERR_INVALID_ARG;
     const int64_t D = (int64_t)num_kv_heads * head_dim;
     if (key_row_stride < D || value_row_stride < D) return NV_ERR_INVALID_ARG;
@@ -700,7 +766,8 @@ extern "C" nv_status nv_paged_attn_decode_store(
                                     stream);
     }
     const FusedStore fs{static_cast<const uint16_t *>(key), key_row_stride,
-                        static_cast<const uint16_t *>(value), value_row_stride, slot_mapping};
+                        static_cast<const uint16_t *>(value), value_row_stride, slot_mapping,
+                        counters};
     return decode_impl(q, k_cache, v_cache, context_lens, block_tables, max_blocks_per_seq, batch,
                        num_heads, num_kv_heads, head_dim, block_size, softmax_scale, workspace,
                        workspace_bytes, out, stream, &fs);
@@ -775,6 +842,7 @@ nv_status decode_impl(const void *q, const void *k_cache, const void *v_cache,
     a.slot_mapping = fs ? fs->slot_mapping : nullptr;
     a.k_pool = fs ? static_cast<uint16_t *>(const_cast<void *>(k_cache)) : nullptr;
     a.v_pool = fs ? static_cast<uint16_t *>(const_cast<void *>(v_cache)) : nullptr;
+    a.counters = fs ? fs->counters : nullptr;
     if (fs) {
         switch (G) {
             case 1: return launch_decode<1, true>(a, batch, stream);

@@ -38,11 +38,15 @@ class DecodeGraphs:
     the block size)."""
 
     def __init__(self, shape: AttnShape, k_cache, v_cache, max_bs: int, max_blocks: int,
-                 scale: float | None = None, fused: bool = False):
+                 scale: float | None = None, fused: bool = False,
+                 merge_in_kernel: bool = True):
         if max_bs < 1 or max_blocks < 1:
             raise ValueError("max_bs and max_blocks must be positive")
         self.shape = shape
         self.fused = fused  # one store+decode launch per layer instead of two
+        # fused only: split rows merged by the split kernel's last workgroup (arrival counters
+        # shared by all layers and buckets; every call leaves them zero), no merge kernel
+        self.merge_in_kernel = fused and merge_in_kernel
         self.k_caches = list(k_cache) if isinstance(k_cache, (list, tuple)) else [k_cache]
         self.v_caches = list(v_cache) if isinstance(v_cache, (list, tuple)) else [v_cache]
         if len(self.k_caches) != len(self.v_caches) or not self.k_caches:
@@ -66,6 +70,8 @@ class DecodeGraphs:
                                                              shape.block_size)
                  for b in buckets(max_bs))
         self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+        self.counters = (nvpaged.decode_counters(max_bs, shape.num_kv_heads, dev)
+                         if self.merge_in_kernel else None)
         self.graphs = {}
         self.pool = None
         for bs in reversed(buckets(max_bs)):
@@ -86,7 +92,7 @@ class DecodeGraphs:
                     self.q[:bs], self.key[:bs], self.value[:bs], self.slot_mapping[:bs], kc, vc,
                     self.context_lens[:bs], self.block_tables[:bs], s.num_kv_heads,
                     s.block_size, self.scale, workspace=self.workspace,
-                    out=self.out[layer, :bs])
+                    out=self.out[layer, :bs], counters=self.counters)
                 continue
             nvpaged.nv_store_kvcache(self.key[:bs], self.value[:bs], kc, vc,
                                      self.slot_mapping[:bs])

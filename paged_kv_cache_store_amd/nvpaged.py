@@ -56,7 +56,7 @@ def _bind(path: str) -> ctypes.CDLL:
     L.nv_paged_attn_decode.restype = ctypes.c_int
     L.nv_paged_attn_decode_store.argtypes = [_p, _p, _i64, _p, _i64, _p, _p, _p, _i64, _p, _p,
                                              _i32, _i32, _i32, _i32, _i32, _i32, _f32, _p, _sz,
-                                             _p, _p]
+                                             _p, _i64, _p, _p]
     L.nv_paged_attn_decode_store.restype = ctypes.c_int
     L.nv_prepare_prefill.argtypes = [_p, _p, _p, _p, _i32, _i32, _p, _p, _p, _p, _p, _p, _i32,
                                      _p]
@@ -333,9 +333,15 @@ def nv_paged_attn_decode_store(q: torch.Tensor, key: torch.Tensor, value: torch.
                                v_cache: torch.Tensor, context_lens: torch.Tensor,
                                block_tables: torch.Tensor, num_kv_heads: int, block_size: int,
                                softmax_scale: float, workspace: torch.Tensor | None = None,
-                               out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+                               out: torch.Tensor | None = None,
+                               counters: torch.Tensor | None = None,
+                               stream=None) -> torch.Tensor:
     """Store of the decode rows' key/value [B, Hkv, d] at slot_mapping [B], then decode
-    attention of q [B, Hq, d], in one launch; returns out [B, Hq, d] bf16."""
+    attention of q [B, Hq, d], in one launch; returns out [B, Hq, d] bf16.
+
+    ``counters``: optional int32 device tensor of at least B * Hkv entries, all zero (e.g. from
+    ``decode_counters``); given, split rows are merged inside the same launch (no merge
+    kernel), and the call leaves the entries zero again."""
     _dev(q, "q", torch.bfloat16)
     if q.dim() != 3 or not q.is_contiguous():
         raise ValueError("q must be a contiguous [batch, num_heads, head_dim] tensor")
@@ -364,14 +370,27 @@ def nv_paged_attn_decode_store(q: torch.Tensor, key: torch.Tensor, value: torch.
         _dev(out, "out", torch.bfloat16)
         if out.shape != q.shape or not out.is_contiguous():
             raise ValueError("out must be contiguous and shaped like q")
+    cptr, ncnt = 0, 0
+    if counters is not None:
+        _dev(counters, "counters", torch.int32)
+        if not counters.is_contiguous() or counters.numel() < b * num_kv_heads:
+            raise ValueError("counters must be contiguous with at least batch * num_kv_heads entries")
+        cptr, ncnt = counters.data_ptr(), counters.numel()
     _check(_lib.nv_paged_attn_decode_store(
         q.data_ptr(), key.data_ptr(), key.stride(0), value.data_ptr(), value.stride(0),
         slot_mapping.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), ns,
         context_lens.data_ptr(), block_tables.data_ptr(), block_tables.shape[1], b, hq,
         int(num_kv_heads), d, int(block_size), float(softmax_scale), workspace.data_ptr(),
-        workspace.numel() * workspace.element_size(), out.data_ptr(), _stream(stream)),
+        workspace.numel() * workspace.element_size(), cptr, ncnt, out.data_ptr(),
+        _stream(stream)),
         "nv_paged_attn_decode_store")
     return out
+
+
+def decode_counters(max_batch: int, num_kv_heads: int, device) -> torch.Tensor:
+    """Zeroed arrival counters for ``nv_paged_attn_decode_store`` (one per row and kv head, for
+    batches up to max_batch); every call leaves them zero, so they are allocated once."""
+    return torch.zeros(max(1, max_batch * num_kv_heads), dtype=torch.int32, device=device)
 
 
 # ---------------------------------------------------------------- host metadata

@@ -36,6 +36,7 @@ class DeviceStep:
     positions: Optional[torch.Tensor] = None  # int64 [N]: position of each row's token
     out_prefill: Optional[torch.Tensor] = None
     out_decode: Optional[torch.Tensor] = None
+    counters: Optional[torch.Tensor] = None   # int32 [B_dec * Hkv], zero: one-launch decode merge
 
 
 def token_positions(step: Step) -> np.ndarray:
@@ -80,6 +81,7 @@ def prepare_step(shape: AttnShape, step: Step, tensors: StepTensors, device) -> 
         ds.out_prefill = torch.empty_like(tensors.q_prefill)
     if step.decode:
         ds.out_decode = torch.empty_like(tensors.q_decode)
+        ds.counters = nvpaged.decode_counters(len(step.decode), shape.num_kv_heads, device)
     return ds
 
 
@@ -133,8 +135,9 @@ def run_decode(ds: DeviceStep, k_cache, v_cache, scale: float, stream=None) -> N
 
 
 def run_decode_store(ds: DeviceStep, k_cache, v_cache, scale: float, stream=None) -> None:
-    """A decode-only step's store and decode in one launch (the step's rows are all decode
-    rows, one per sequence, in the order of ``context_lens``)."""
+    """A decode-only step's store and decode in one launch, split rows merged in the same
+    launch (the step's rows are all decode rows, one per sequence, in the order of
+    ``context_lens``)."""
     if ds.context_lens is None:
         return
     s = ds.shape
@@ -143,7 +146,7 @@ def run_decode_store(ds: DeviceStep, k_cache, v_cache, scale: float, stream=None
                                        v_cache, ds.context_lens, ds.decode_tables,
                                        s.num_kv_heads, s.block_size, scale,
                                        workspace=ds.workspace, out=ds.out_decode,
-                                       stream=stream)
+                                       counters=ds.counters, stream=stream)
 
 
 def run_step(ds: DeviceStep, k_cache, v_cache, scale: Optional[float] = None, stream=None):

@@ -172,22 +172,29 @@ def test_decode_store_argument_errors(nv):
     null = None
     # key null, key row stride below Hkv * d, negative num_slots, null slot_mapping
     assert L.nv_paged_attn_decode_store(1, null, 1024, 1, 1024, 1, 1, 1, 100, 1, 1, 3, 4, 16, 8,
-                                        128, 256, 0.1, 256, 1 << 20, 1, null) == -1
+                                        128, 256, 0.1, 256, 1 << 20, null, 0, 1, null) == -1
     assert L.nv_paged_attn_decode_store(1, 1, 512, 1, 1024, 1, 1, 1, 100, 1, 1, 3, 4, 16, 8,
-                                        128, 256, 0.1, 256, 1 << 20, 1, null) == -1
+                                        128, 256, 0.1, 256, 1 << 20, null, 0, 1, null) == -1
     assert L.nv_paged_attn_decode_store(1, 1, 1024, 1, 1024, 1, 1, 1, -1, 1, 1, 3, 4, 16, 8,
-                                        128, 256, 0.1, 256, 1 << 20, 1, null) == -1
+                                        128, 256, 0.1, 256, 1 << 20, null, 0, 1, null) == -1
     assert L.nv_paged_attn_decode_store(1, 16, 1024, 16, 1024, null, 16, 16, 100, 1, 1, 3, 4,
-                                        16, 8, 128, 256, 0.1, 256, 1 << 20, 1, null) == -1
+                                        16, 8, 128, 256, 0.1, 256, 1 << 20, null, 0, 1, null) == -1
     # decode-side errors surface unchanged (16-byte aligned dummies: the fused path is taken)
     assert L.nv_paged_attn_decode_store(16, 16, 1024, 16, 1024, 16, 16, 16, 100, 16, 16, 3, 4,
-                                        16, 8, 128, 256, 0.0, 256, 1 << 20, 16, null) == -1
+                                        16, 8, 128, 256, 0.0, 256, 1 << 20, null, 0, 16, null) == -1
     assert L.nv_paged_attn_decode_store(16, 16, 1024, 16, 1024, 16, 16, 16, 100, 16, 16, 3, 4,
-                                        16, 8, 64, 256, 0.1, 256, 1 << 20, 16, null) == -2
+                                        16, 8, 64, 256, 0.1, 256, 1 << 20, null, 0, 16, null) == -2
     # empty batch: nothing to do
     assert L.nv_paged_attn_decode_store(null, null, 1024, null, 1024, null, null, null, 0, null,
-                                        null, 3, 0, 16, 8, 128, 256, 0.1, null, 0, null,
-                                        null) == 0
+                                        null, 3, 0, 16, 8, 128, 256, 0.1, null, 0, null, 0,
+                                        null, null) == 0
+    # arrival counters shorter than batch * num_kv_heads (4 * 8), or not 4-byte aligned
+    assert L.nv_paged_attn_decode_store(16, 16, 1024, 16, 1024, 16, 16, 16, 100, 16, 16, 3, 4,
+                                        16, 8, 128, 256, 0.1, 256, 1 << 20, 64, 31, 16,
+                                        null) == -1
+    assert L.nv_paged_attn_decode_store(16, 16, 1024, 16, 1024, 16, 16, 16, 100, 16, 16, 3, 4,
+                                        16, 8, 128, 256, 0.1, 256, 1 << 20, 66, 32, 16,
+                                        null) == -1
 
 
 def test_decode_split_choice(nv):

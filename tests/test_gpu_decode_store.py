@@ -1,8 +1,10 @@
 """GPU parity of the one-launch store + decode (nv_paged_attn_decode_store).
 
 It must equal nv_store_kvcache followed by nv_paged_attn_decode bit for bit (pools and
-outputs), for split and unsplit launches, padding rows and several shapes and block sizes;
-and, on its own, match the oracle's store (bit-exact pools) and decode (attention bound).
+outputs), for split and unsplit launches, padding rows and several shapes and block sizes,
+with split rows merged by the merge kernel or inside the launch (arrival counters, which
+every call must leave zero); and, on its own, match the oracle's store (bit-exact pools) and
+decode (attention bound).
 """
 import numpy as np
 import pytest
@@ -24,8 +26,9 @@ CASES = [  # shape, decode rows, max context, padding rows
 ]
 
 
+@pytest.mark.parametrize("merge", ["merge_kernel", "in_kernel"])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[0].num_heads}q{c[0].num_kv_heads}kv_bs{c[0].block_size}_B{c[1]}")
-def test_fused_equals_store_then_decode(case):
+def test_fused_equals_store_then_decode(case, merge):
     shape, n, max_len, pad = case
     w = workloads.random_workload(60 + n, shape, 0, n, max_len=max_len, pad_rows=pad)
     print(f"[decode_store] {shape} rows={n}+{pad}", flush=True)
@@ -40,11 +43,15 @@ def test_fused_equals_store_then_decode(case):
     # fused, into an output that starts as NaN
     t = ds_b.tensors
     out = torch.full_like(t.q_decode, float("nan"))
+    cnt = (nvpaged.decode_counters(t.q_decode.shape[0], shape.num_kv_heads, "cuda")
+           if merge == "in_kernel" else None)
     nvpaged.nv_paged_attn_decode_store(t.q_decode, t.key, t.value, ds_b.slot_mapping,
                                        run_b.k_cache, run_b.v_cache, ds_b.context_lens,
                                        ds_b.decode_tables, shape.num_kv_heads, shape.block_size,
-                                       scale, out=out)
+                                       scale, out=out, counters=cnt)
     torch.cuda.synchronize()
+    if cnt is not None:
+        assert int(cnt.abs().sum()) == 0, "arrival counters not returned to zero"
     assert np.array_equal(bits(run_a.k_cache), bits(run_b.k_cache))
     assert np.array_equal(bits(run_a.v_cache), bits(run_b.v_cache))
     assert np.array_equal(bits(ds_a.out_decode), bits(out)), "outputs differ"
@@ -53,6 +60,31 @@ def test_fused_equals_store_then_decode(case):
     check_pools_bit_exact(run_b, "fused store")
     ids, ref = run_b.oracle_decode(0)
     print(assert_attn_close(out[ids], ref, "fused decode"))
+
+
+def test_in_kernel_merge_reuses_counters():
+    """One zeroed counter array serves a run of calls of different batches and split counts
+    (contexts up to 4000 keys in 128-key splits: up to 32 partials per row), each call
+    bitwise equal to the same call with the merge kernel, the counters zero after each."""
+    shape = workloads.QWEN3_0_6B
+    cnt = nvpaged.decode_counters(64, shape.num_kv_heads, "cuda")
+    for i, (n, max_len) in enumerate([(2, 4000), (7, 3000), (1, 4000), (40, 2500), (3, 600),
+                                      (2, 4000)] * 2):
+        w = workloads.random_workload(300 + i, shape, 0, n, max_len=max_len, pad_rows=1)
+        print(f"[decode_store counters] call {i} rows={n}+1 max_len={max_len}", flush=True)
+        outs = []
+        for c in (None, cnt):
+            run = Run(w)
+            ds = gstep.prepare_step(shape, w.steps[0], run.tensors[0], "cuda")
+            t = ds.tensors
+            o = nvpaged.nv_paged_attn_decode_store(t.q_decode, t.key, t.value, ds.slot_mapping,
+                                                   run.k_cache, run.v_cache, ds.context_lens,
+                                                   ds.decode_tables, shape.num_kv_heads,
+                                                   shape.block_size, run.scale, counters=c)
+            torch.cuda.synchronize()
+            outs.append(bits(o).copy())
+        assert np.array_equal(outs[0], outs[1]), f"call {i}: in-kernel merge differs"
+        assert int(cnt.abs().sum()) == 0, f"call {i}: counters not returned to zero"
 
 
 def test_fused_unaligned_rows_fall_back():
@@ -85,12 +117,12 @@ def test_fused_graph_replay_matches_two_call_graph():
     shape = workloads.QWEN3_0_6B
     w = workloads.config_decode_small()
     res = []
-    for fused in (False, True):
+    for fused, in_kernel in ((False, False), (True, False), (True, True)):
         run = Run(w)
         ds = gstep.prepare_step(shape, w.steps[0], run.tensors[0], "cuda")
         dg = graphs.DecodeGraphs(shape, run.k_cache, run.v_cache, max_bs=8,
                                  max_blocks=ds.decode_tables.shape[1], scale=run.scale,
-                                 fused=fused)
+                                 fused=fused, merge_in_kernel=in_kernel)
         t = ds.tensors
         outs = []
         for _ in range(3):
@@ -98,8 +130,11 @@ def test_fused_graph_replay_matches_two_call_graph():
                        ds.decode_tables)
             torch.cuda.synchronize()
             outs.append(bits(o).copy())
+        if dg.counters is not None:
+            assert int(dg.counters.abs().sum()) == 0
         res.append((outs, bits(run.k_cache).copy(), bits(run.v_cache).copy()))
-    (o0, k0, v0), (o1, k1, v1) = res
-    for a, b in zip(o0, o1):
-        assert np.array_equal(a, b)
-    assert np.array_equal(k0, k1) and np.array_equal(v0, v1)
+    o0, k0, v0 = res[0]
+    for o1, k1, v1 in res[1:]:
+        for a, b in zip(o0, o1):
+            assert np.array_equal(a, b)
+        assert np.array_equal(k0, k1) and np.array_equal(v0, v1)

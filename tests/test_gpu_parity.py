@@ -48,7 +48,10 @@ def test_config_prefill_varlen():
 SHAPES = [workloads.AttnShape(16, 8, 128, 256), workloads.AttnShape(32, 8, 128, 256),
           workloads.AttnShape(8, 8, 128, 64), workloads.AttnShape(12, 4, 128, 48),
           workloads.AttnShape(16, 2, 128, 16), workloads.AttnShape(8, 4, 128, 512),
-          workloads.AttnShape(10, 2, 128, 128)]
+          workloads.AttnShape(10, 2, 128, 128),
+          # decode grid: kv heads of a (sequence, split) go to an XCD gcd(Hkv, G) at a time;
+          # these split each pair's heads into 3 units of 2 (G = 4) and 3 units of 1 (G = 7)
+          workloads.AttnShape(24, 6, 128, 32), workloads.AttnShape(21, 3, 128, 64)]
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"{s.num_heads}q{s.num_kv_heads}kv_bs{s.block_size}")

@@ -173,6 +173,39 @@ def norm_rope_store_part(shape, dsteps, k_cache, v_cache, iters: int) -> dict:
             "bytes": nbytes}
 
 
+def store_queued(dsteps, k_cache, v_cache, nbytes: int, inner: int = 20, reps: int = 5) -> dict:
+    """The step's store calls launched back to back, `inner` per HIP-event-timed region, with
+    the GPU held busy by a sleep kernel while they are queued: the store kernel's own rate,
+    without the launch gap that the single event-timed call of the step loop includes (at
+    this size the gap is a third of that figure). Storing the same rows again is
+    idempotent."""
+    from paged_kv_cache_store_amd import step as gstep
+
+    def once():
+        for ds in dsteps:
+            gstep.run_store(ds, k_cache, v_cache)
+
+    for _ in range(3):
+        once()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(2_000_000)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(inner):
+            once()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) * 1e3 / inner)
+    us = sorted(ts)[len(ts) // 2]
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"us": round(us, 2), "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "calls_per_region": inner}
+
+
 def small_decode_latency(dev, iters: int, layers: int = 28) -> dict:
     """Time of one small decode step (4 sequences + 2 padding rows, Qwen3-0.6B shape) through
     `layers` attention layers, each with its own pool: store + decode launched eagerly per
@@ -380,6 +413,7 @@ def main():
         res["parts"]["norm_rope_store"] = norm_rope_store_part(shape, dsteps, k_cache, v_cache,
                                                                args.steps)
         res["parts"]["decode_small_step"] = small_decode_latency(dev, max(20, args.steps))
+        res["parts"]["store_queued"] = store_queued(dsteps, k_cache, v_cache, sto_bytes)
     if packed_ms:
         tf = packed_flops / (packed_ms * 1e-3) / 1e12
         res["parts"]["prefill_packed"] = {"ms": round(packed_ms, 4), "TFLOP/s": round(tf, 1),

@@ -197,7 +197,12 @@ nv_status nv_qk_norm_rope_store(const void *qkv, int64_t qkv_row_stride,
  *   softmax_scale positive and finite; the engine passes head_dim ** -0.5.
  *   out           device bf16 [batch, num_heads, head_dim] contiguous.
  * Supported: head_dim == 128, num_heads % num_kv_heads == 0, (num_heads / num_kv_heads) <= 8,
- * block_size >= 1.
+ * block_size >= 1. Errors (nothing launched): NV_ERR_INVALID_ARG (null pointer, negative or
+ * zero sizes, Hq % Hkv != 0, scale not positive and finite), NV_ERR_UNSUPPORTED (head_dim, a
+ * group above 8, batch or num_kv_heads above 65535, more than 65535 splits, or a grid of
+ * 2^31 workgroups or more),
+ * NV_ERR_WORKSPACE (workspace smaller than required or not 256-byte aligned); NV_ERR_LAUNCH
+ * if the launch itself fails. An empty batch returns NV_OK.
  * ------------------------------------------------------------------------------------------ */
 size_t nv_paged_attn_decode_workspace_size(int32_t batch, int32_t num_heads,
                                            int32_t num_kv_heads, int32_t head_dim,

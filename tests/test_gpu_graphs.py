@@ -23,9 +23,12 @@ def _decode_batch(rng, pool, bs, max_ctx, block_size):
     return seqs
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["two_call", "fused"])
 @pytest.mark.parametrize("shape", [workloads.QWEN3_0_6B, workloads.QWEN3_8B],
                          ids=lambda s: f"{s.num_heads}q{s.num_kv_heads}kv")
-def test_graph_replay_matches_eager_and_oracle(shape):
+def test_graph_replay_matches_eager_and_oracle(shape, fused):
+    """fused: one store+decode launch per layer, split rows merged in the same launch through
+    arrival counters shared by every bucket (contexts up to 700 split into 128-key pieces)."""
     dev = torch.device("cuda")
     bsz = shape.block_size
     max_bs, max_ctx = 48, 700
@@ -41,7 +44,7 @@ def test_graph_replay_matches_eager_and_oracle(shape):
     k_host, v_host = bits(k_cache).copy(), bits(v_cache).copy()
     scale = shape.head_dim ** -0.5
     print(f"[graphs] {shape}: capturing buckets {graphs.buckets(max_bs)}", flush=True)
-    dg = graphs.DecodeGraphs(shape, k_cache, v_cache, max_bs, max_blocks, scale)
+    dg = graphs.DecodeGraphs(shape, k_cache, v_cache, max_bs, max_blocks, scale, fused=fused)
     scratch = torch.randn(512, 512, device=dev)
     for step, bs in enumerate(batches):
         seqs = _decode_batch(rng, pool, bs, max_ctx, bsz)
@@ -61,6 +64,13 @@ def test_graph_replay_matches_eager_and_oracle(shape):
         torch.cuda.synchronize()
         assert torch.equal(out_g.view(torch.int16), out_e.view(torch.int16)), f"step {step}"
         assert torch.count_nonzero(pad).item() == 0, "padding rows must output zeros"
+        # The plain decode (merge kernel) over the pool the replay stored into: same bits.
+        out_p = nvpaged.nv_paged_attn_decode(args[0], k_cache, v_cache, args[4], args[5],
+                                             shape.num_kv_heads, bsz, scale)
+        torch.cuda.synchronize()
+        assert torch.equal(out_g.view(torch.int16), out_p.view(torch.int16)), f"step {step}"
+        if dg.counters is not None:
+            assert int(dg.counters.abs().sum()) == 0, "arrival counters must return to zero"
         # Oracle: its own metadata, its own store into the host pool, fp64 attention.
         om = meta.prepare_decode(seqs, bsz)
         oracle.store_kvcache(bits(kv[:, 0]).reshape(bs, D), bits(kv[:, 1]).reshape(bs, D),

@@ -191,6 +191,64 @@ def norm_rope_store_part(shape, dsteps, k_cache, v_cache, iters: int) -> dict:
             "queued_frac_hbm_peak": round(qgbs / HBM_PEAK_GBS, 4)}
 
 
+def percentiles(times_ms) -> dict:
+    """p10 / p50 / p90 of per-step times (ms); the means above give the rates."""
+    s = sorted(times_ms)
+    at = lambda p: s[min(len(s) - 1, int(round(p / 100 * (len(s) - 1))))]
+    return {"ms_p10": round(at(10), 4), "ms_p50": round(at(50), 4), "ms_p90": round(at(90), 4)}
+
+
+def copy_ceiling(dev, nbytes: int = 1 << 30, reps: int = 10) -> dict:
+    """A plain device copy of `nbytes` (torch copy_ of a contiguous bf16 buffer): bytes read
+    plus bytes written per second, the practical ceiling a streaming kernel on this HBM can
+    reach, beside the published peak. Median over `reps` HIP-event-timed copies."""
+    x = torch.ones(nbytes // 2, dtype=torch.bfloat16, device=dev)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        y.copy_(x)
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    t = sorted(ts)[len(ts) // 2]
+    gbs = 2 * nbytes / (t * 1e-3) / 1e9
+    del x, y
+    return {"ms": round(t, 4), "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "bytes_read": nbytes, "bytes_written": nbytes}
+
+
+def read_ceiling(dev, nbytes: int = 4 << 30, reps: int = 10) -> dict:
+    """The library's streaming-read probe (nv_probe_stream_read) over `nbytes`, far larger
+    than the caches: the HBM read rate a plain kernel reaches, the practical ceiling for the
+    decode (read-only traffic). Median over `reps` HIP-event-timed calls."""
+    from paged_kv_cache_store_amd import nvpaged
+    x = torch.ones(nbytes // 2, dtype=torch.bfloat16, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        nvpaged.nv_probe_stream_read(x, sink)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        nvpaged.nv_probe_stream_read(x, sink)
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    t = sorted(ts)[len(ts) // 2]
+    gbs = nbytes / (t * 1e-3) / 1e9
+    del x, sink
+    return {"ms": round(t, 4), "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "bytes_read": nbytes}
+
+
 def store_queued(dsteps, k_cache, v_cache, nbytes: int, inner: int = 20, reps: int = 5) -> dict:
     """The step's store calls launched back to back, `inner` per HIP-event-timed region, with
     the GPU held busy by a sleep kernel while they are queued: the store kernel's own rate,
@@ -370,6 +428,10 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = {n: sum(a.elapsed_time(b) for a, b in ev[n]) / args.steps for n in names}
+    # Per-step times (the step's calls of each part summed) for percentiles.
+    k = len(dsteps)
+    per_step = {n: [sum(a.elapsed_time(b) for a, b in ev[n][i * k:(i + 1) * k])
+                    for i in range(args.steps)] for n in names}
 
     # The same fresh prompts through the packed (no block table) prefill path, timed apart.
     packed = [ds for ds in dsteps if ds.cu_seqlens_q is not None
@@ -415,12 +477,13 @@ def main():
                    "prefill_tokens": w.steps[0].num_prefill_tokens, "seed": w.seed},
         "parts": {
             "store": {"ms": round(ms["store"], 4), "GB/s": round(sto_gbs, 1),
-                      "bytes": sto_bytes},
+                      "bytes": sto_bytes, **percentiles(per_step["store"])},
             "prefill": {"ms": round(ms["prefill"], 4), "TFLOP/s": round(pre_tflops, 1),
                         "frac_bf16_peak": round(pre_tflops / BF16_PEAK_TFLOPS, 4),
-                        "flops": pre_flops},
+                        "flops": pre_flops, **percentiles(per_step["prefill"])},
             "decode": {"ms": round(ms["decode"], 4), "GB/s": round(dec_gbs, 1),
-                       "frac_hbm_peak": round(dec_gbs / HBM_PEAK_GBS, 4), "bytes": dec_bytes},
+                       "frac_hbm_peak": round(dec_gbs / HBM_PEAK_GBS, 4), "bytes": dec_bytes,
+                       **percentiles(per_step["decode"])},
         },
         "roofline": {"bound": "hbm", "kernel": "decode (split kernel, + merge kernel when a row is split)",
                      "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -432,6 +495,11 @@ def main():
                                                                args.steps)
         res["parts"]["decode_small_step"] = small_decode_latency(dev, max(20, args.steps))
         res["parts"]["store_queued"] = store_queued(dsteps, k_cache, v_cache, sto_bytes)
+        res["parts"]["copy_ceiling"] = copy_ceiling(dev)
+        res["parts"]["read_ceiling"] = read_ceiling(dev)
+        res["roofline"]["measured_read_ceiling_GB/s"] = res["parts"]["read_ceiling"]["GB/s"]
+        res["roofline"]["frac_of_measured_ceiling"] = round(
+            dec_gbs / res["parts"]["read_ceiling"]["GB/s"], 4)
     if packed_ms:
         tf = packed_flops / (packed_ms * 1e-3) / 1e12
         res["parts"]["prefill_packed"] = {"ms": round(packed_ms, 4), "TFLOP/s": round(tf, 1),

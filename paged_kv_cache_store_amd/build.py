@@ -1,4 +1,5 @@
-"""Builds libnvpaged.so, the gfx950 HIP library behind include/nv_paged.h, in-tree.
+"""Builds libnvpaged.so, the gfx950 HIP library behind include/nv_paged.h (and the measurement
+helper of include/nv_probe.h), in-tree.
 
 Every source is compiled for gfx950 only, with packed-fp32 instruction selection disabled, then
 linked into one shared library next to this file.
@@ -16,7 +17,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libnvpaged.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["store.hip", "decode.hip", "prefill.hip", "norm_rope_store.hip", "host_meta.cpp"]
+SOURCES = ["store.hip", "decode.hip", "prefill.hip", "norm_rope_store.hip", "probe_read.hip",
+           "host_meta.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC,

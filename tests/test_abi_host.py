@@ -24,7 +24,9 @@ def nv():
 
 
 def test_exports_every_declared_symbol(nv):
-    header = open(os.path.join(ROOT, "include", "nv_paged.h")).read()
+    inc = os.path.join(ROOT, "include")
+    header = "".join(open(os.path.join(inc, f)).read() for f in sorted(os.listdir(inc))
+                     if f.endswith(".h"))
     declared = set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(nv_\w+)\s*\(", header, re.M))
     assert declared == set(nv.EXPORTS)
     for name in declared:
@@ -274,3 +276,13 @@ def test_token_positions_match_oracle(name):
         if st.decode:
             parts.append(meta.prepare_decode(st.decode, w.shape.block_size)["positions"])
         assert np.array_equal(gstep.token_positions(st), np.concatenate(parts))
+
+
+def test_probe_argument_errors(nv):
+    """The streaming-read probe rejects bad arguments before launching anything."""
+    L = nv.lib()
+    assert L.nv_probe_stream_read(None, 1024, 64, None) == -1
+    assert L.nv_probe_stream_read(64, 1024, None, None) == -1
+    assert L.nv_probe_stream_read(64, 1000, 64, None) == -1   # not a multiple of 16
+    assert L.nv_probe_stream_read(64, 0, 64, None) == -1
+    assert L.nv_probe_stream_read(72, 1024, 64, None) == -1   # src not 16-byte aligned

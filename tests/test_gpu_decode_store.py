@@ -87,6 +87,32 @@ def test_in_kernel_merge_reuses_counters():
         assert int(cnt.abs().sum()) == 0, f"call {i}: counters not returned to zero"
 
 
+def test_in_kernel_merge_stress():
+    """300 one-launch calls on one workload with up to 32 partials per row, each on a random
+    prefix of its rows, sharing one counter array: every output equals the merge-kernel
+    result of the same call bit for bit (the split length depends on the batch, so the
+    reference is taken per call), and the counters end at zero."""
+    shape = workloads.QWEN3_8B
+    w = workloads.random_workload(777, shape, 0, 24, max_len=4000, pad_rows=2)
+    run = Run(w)
+    ds = gstep.prepare_step(shape, w.steps[0], run.tensors[0], "cuda")
+    t = ds.tensors
+    n_all = t.q_decode.shape[0]
+    args = lambda n: (t.q_decode[:n], t.key[:n], t.value[:n], ds.slot_mapping[:n], run.k_cache,
+                      run.v_cache, ds.context_lens[:n], ds.decode_tables[:n], shape.num_kv_heads,
+                      shape.block_size, run.scale)
+    cnt = nvpaged.decode_counters(n_all, shape.num_kv_heads, "cuda")
+    rng = np.random.default_rng(5)
+    print(f"[decode_store stress] rows {n_all}, 300 calls", flush=True)
+    for i in range(300):
+        n = int(rng.integers(1, n_all + 1))
+        ref = nvpaged.nv_paged_attn_decode_store(*args(n))  # merge kernel
+        o = nvpaged.nv_paged_attn_decode_store(*args(n), counters=cnt)
+        assert np.array_equal(bits(o), bits(ref)), f"call {i} (rows {n}) differs"
+    torch.cuda.synchronize()
+    assert int(cnt.abs().sum()) == 0
+
+
 def test_fused_unaligned_rows_fall_back():
     """A value view whose rows are not 16-byte aligned takes the two-call path, same result."""
     shape = workloads.AttnShape(8, 2, 128, 64)

@@ -19,6 +19,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixed_8b]
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -413,6 +414,10 @@ def main():
 
     names = ("store", "prefill", "decode")
     ev = {n: [] for n in names}
+    # No Python garbage collection inside the timed region: a collection pass between an
+    # event's record and its launch would stall the GPU and land in that part's time.
+    gc.collect()
+    gc.disable()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         for ds in dsteps:
@@ -427,6 +432,7 @@ def main():
                 ev[n].append((a, b))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    gc.enable()
     ms = {n: sum(a.elapsed_time(b) for a, b in ev[n]) / args.steps for n in names}
     # Per-step times (the step's calls of each part summed) for percentiles.
     k = len(dsteps)

@@ -250,6 +250,38 @@ def read_ceiling(dev, nbytes: int = 4 << 30, reps: int = 10) -> dict:
             "bytes_read": nbytes}
 
 
+def prefill_queued(dsteps, k_cache, v_cache, scale: float, flops: int, inner: int = 10,
+                   reps: int = 5) -> dict:
+    """The step's prefill calls launched back to back behind a sleep kernel (as for
+    `store_queued`): the kernel's own rate, without the host time between the start event and
+    the launch that a single call in the step loop can include."""
+    from paged_kv_cache_store_amd import step as gstep
+
+    def once():
+        for ds in dsteps:
+            gstep.run_prefill(ds, k_cache, v_cache, scale)
+
+    for _ in range(3):
+        once()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(2_000_000)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(inner):
+            once()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) * 1e3 / inner)
+    us = sorted(ts)[len(ts) // 2]
+    tf = flops / (us * 1e-6) / 1e12
+    return {"us": round(us, 2), "TFLOP/s": round(tf, 1), "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
+            "calls_per_region": inner}
+
+
 def store_queued(dsteps, k_cache, v_cache, nbytes: int, inner: int = 20, reps: int = 5) -> dict:
     """The step's store calls launched back to back, `inner` per HIP-event-timed region, with
     the GPU held busy by a sleep kernel while they are queued: the store kernel's own rate,
@@ -501,6 +533,9 @@ def main():
                                                                args.steps)
         res["parts"]["decode_small_step"] = small_decode_latency(dev, max(20, args.steps))
         res["parts"]["store_queued"] = store_queued(dsteps, k_cache, v_cache, sto_bytes)
+        if pre_flops:
+            res["parts"]["prefill_queued"] = prefill_queued(dsteps, k_cache, v_cache, scale,
+                                                            pre_flops)
         res["parts"]["copy_ceiling"] = copy_ceiling(dev)
         res["parts"]["read_ceiling"] = read_ceiling(dev)
         res["roofline"]["measured_read_ceiling_GB/s"] = res["parts"]["read_ceiling"]["GB/s"]

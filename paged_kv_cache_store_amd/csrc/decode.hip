@@ -66,7 +66,7 @@
 #define NV_DECODE_MAX_SPLIT 8192     // longest split (keys)
 #endif
 #ifndef NV_DECODE_TARGET_ITEMS
-#define NV_DECODE_TARGET_ITEMS 2048  // work items the split size aims for
+#define NV_DECODE_TARGET_ITEMS 4096  // work items the split size aims for
 #endif
 #ifndef NV_DECODE_PV_DOT2
 #define NV_DECODE_PV_DOT2 1     // P.V as bf16-pair dot products over two keys at a time
@@ -83,6 +83,9 @@
 #endif
 #ifndef NV_DECODE_XCD_HEADS
 #define NV_DECODE_XCD_HEADS 0   // order 2: kv heads kept together per XCD (0: the group size G)
+#endif
+#ifndef NV_DECODE_ONE_GO_GROUPS
+#define NV_DECODE_ONE_GO_GROUPS 768  // grids up to this many workgroups keep splits together
 #endif
 #ifndef NV_DECODE_MIN_WAVES
 #define NV_DECODE_MIN_WAVES 1   // occupancy hint: waves per SIMD the register budget must allow
@@ -119,6 +122,8 @@ struct DecodeArgs {
     int32_t split_keys;
     int32_t max_splits;
     int32_t n_pairs;  // batch * max_splits
+    int32_t batch;
+    int32_t splits_together;  // 1: a sequence's splits are consecutive pairs (small grids)
     int32_t xcd_heads;  // kv heads of one pair kept together on one XCD (divides num_kv_heads)
     float scale_log2;  // softmax_scale * log2(e)
     float rescale_slack;  // raw-score growth of a running max tolerated without a rescale
@@ -232,8 +237,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
     const int per_pair = a.num_kv_heads / hg;
     if (unit >= a.n_pairs * per_pair) return;
     const int g = (unit % per_pair) * hg + local % hg;
+    // Pair numbering. A grid that runs in one go numbers a sequence's splits consecutively
+    // (they start together, which matters when the last one merges). A larger grid numbers
+    // sequences fastest: every sequence's first (longest) split is dispatched before any
+    // second one, and each split index spreads over all XCDs.
     const int pair = unit / per_pair;
-    const int s = pair % a.max_splits, b = pair / a.max_splits;
+    const int b = a.splits_together ? pair / a.max_splits : pair % a.batch;
+    const int s = a.splits_together ? pair % a.max_splits : pair / a.batch;
 #elif NV_DECODE_HEAD_MAJOR
     const int g = blockIdx.x, s = blockIdx.y, b = blockIdx.z;
 #else
@@ -858,8 +868,15 @@ nv_status decode_impl(const void *q, const void *k_cache, const void *v_cache,
     if ((int64_t)batch * splits * num_kv_heads + 8 * (int64_t)num_kv_heads > INT32_MAX)
         return NV_ERR_UNSUPPORTED;  // grid size
     a.n_pairs = (int32_t)(batch * splits);
+    a.batch = batch;
     a.xcd_heads = std::gcd(num_kv_heads, NV_DECODE_XCD_HEADS > 0 ? (int32_t)NV_DECODE_XCD_HEADS
                                                                   : num_heads / num_kv_heads);
+    {
+        // Workgroups of the 1D grid; up to 3 per CU (the register budget of G <= 4) it runs
+        // in one go on the 256 CUs.
+        const int64_t units = (int64_t)a.n_pairs * (num_kv_heads / a.xcd_heads);
+        a.splits_together = 8 * ((units + 7) / 8) * a.xcd_heads <= NV_DECODE_ONE_GO_GROUPS;
+    }
     const size_t rows = (size_t)batch * num_heads * splits;
     const size_t ml_bytes = (rows * 2 * sizeof(float) + 255) / 256 * 256;
     a.ws_ml = need ? static_cast<float *>(workspace) : nullptr;

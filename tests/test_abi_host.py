@@ -201,11 +201,11 @@ def test_decode_store_argument_errors(nv):
 
 def test_decode_split_choice(nv):
     # Small batches get short splits so the chip fills; large ones get long splits (few
-    # partial results): 2048 (sequence, kv head) pairs or more run unsplit up to 8192 keys.
+    # partial results): 4096 (sequence, kv head) pairs or more run unsplit up to 8192 keys.
     assert nv.nv_paged_attn_decode_split_keys(6, 8, 3, 256) == 128
-    assert nv.nv_paged_attn_decode_split_keys(256, 8, 16, 256) == 8192
+    assert nv.nv_paged_attn_decode_split_keys(256, 8, 16, 256) == 2048  # 2048 pairs x 2
     assert nv.nv_paged_attn_decode_split_keys(512, 8, 16, 256) == 8192
-    assert nv.nv_paged_attn_decode_split_keys(64, 8, 16, 256) == 1024  # 512 pairs x 4 splits
+    assert nv.nv_paged_attn_decode_split_keys(64, 8, 16, 256) == 512  # 512 pairs x 8 splits
     assert nv.nv_paged_attn_decode_workspace_size(512, 32, 8, 128, 16, 256) == 0
     prev = None
     for b in (1, 3, 17, 100, 600, 5000):

@@ -22,7 +22,7 @@ CASES = [  # shape, decode rows, max context, padding rows
     (workloads.QWEN3_8B, 9, 3000, 1),
     (workloads.AttnShape(12, 4, 128, 16), 7, 900, 2),
     (workloads.AttnShape(32, 4, 128, 48), 5, 700, 0),
-    (workloads.AttnShape(16, 8, 128, 256), 300, 1500, 4),  # 2400 pairs: unsplit, no merge
+    (workloads.AttnShape(16, 8, 128, 256), 508, 1500, 4),  # 4096 pairs: unsplit, no merge
 ]
 
 

@@ -95,20 +95,20 @@ def test_unsplit_decode_with_padding_rows():
     rows' zeros come from the split kernel, over an output buffer that starts as NaN."""
     from paged_kv_cache_store_amd import nvpaged, step as gstep
     shape = workloads.AttnShape(16, 8, 128, 256)
-    w = workloads.random_workload(31, shape, 0, 294, max_len=1500, pad_rows=6)
-    assert nvpaged.nv_paged_attn_decode_split_keys(300, 8, 6, 256) >= 1536
+    w = workloads.random_workload(31, shape, 0, 506, max_len=1500, pad_rows=6)
+    assert nvpaged.nv_paged_attn_decode_split_keys(512, 8, 6, 256) >= 1536
     run = Run(w)
     ds = gstep.prepare_step(shape, w.steps[0], run.tensors[0], "cuda")
     assert ds.decode_tables.shape[1] * 256 <= nvpaged.nv_paged_attn_decode_split_keys(
-        300, 8, ds.decode_tables.shape[1], 256)
+        512, 8, ds.decode_tables.shape[1], 256)
     ds.out_decode.fill_(float("nan"))
-    print("[unsplit] 294 rows + 6 padding rows", flush=True)
+    print("[unsplit] 506 rows + 6 padding rows", flush=True)
     gstep.run_step(ds, run.k_cache, run.v_cache, run.scale)
     torch.cuda.synchronize()
-    assert torch.count_nonzero(ds.out_decode[294:]).item() == 0
+    assert torch.count_nonzero(ds.out_decode[506:]).item() == 0
     assert torch.isfinite(ds.out_decode.float()).all()
     run.oracle_store(0)
-    ids, ref = run.oracle_decode(0, list(range(0, 294, 7)))
+    ids, ref = run.oracle_decode(0, list(range(0, 506, 11)))
     print(assert_attn_close(ds.out_decode[ids], ref, "unsplit decode"))
 
 

@@ -33,10 +33,9 @@
 //    out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, M = max_s m_s.
 //    When no row can have a second split the merge kernel is not launched; rows without keys
 //    get their zeros from the split kernel.
-//  - Splits are as long as possible (up to 8192 keys) while the launch keeps >= 2048 work
-//    items: partial results written into the read stream cost far more than their bytes, so
-//    e.g. the Qwen3-8B step (512 sequences x 8 kv heads, contexts <= 4096) runs unsplit
-//    (measured +9% over 2048-key splits).
+//  - Splits are as long as possible (up to 8192 keys) while the launch keeps >= 4096 work
+//    items, e.g. the Qwen3-8B step (512 sequences x 8 kv heads, contexts <= 4096) runs
+//    unsplit and the Qwen3-0.6B decode of 256 sequences in two 2048-key splits.
 //  - Scores are kept in log2 units (scale * log2(e) folded in; exp2 is the hardware exp).
 //  - Grid order (XCD-aware): the hardware deals consecutive workgroup ids round-robin to the
 //    8 XCDs. A unit of gcd(Hkv, G) consecutive kv heads of one (sequence, split) runs as
@@ -44,7 +43,12 @@
 //    XCD reads contiguous 256*G-byte stretches of the same pool rows at the same time.
 //    Measured +2% (Qwen3-0.6B, 256 sequences) and +4% (Qwen3-8B step) over the kv-head-
 //    fastest 3D grid, which gave each XCD one head's 256-byte slice of every row; that order
-//    was itself +9% on the 8B decode over split-major order.
+//    was itself +9% on the 8B decode over split-major order. (Sequence, split) pairs are
+//    numbered sequence fastest when the grid is larger than the chip holds at once (every
+//    first split is dispatched before any second one, and each split index spreads over all
+//    XCDs: numbered split fastest, the first splits sat on a fixed half of the XCDs), and
+//    split fastest when it runs in one go (a sequence's splits start together, which the
+//    in-kernel merge of small steps prefers).
 //  - One-launch store + decode (nv_paged_attn_decode_store, a decode step's two calls): the
 //    workgroup holding a row's new token loads that key's row from the step's new K/V rows and
 //    writes it to the pools; with arrival counters the last workgroup of a split row to finish

@@ -19,8 +19,9 @@
 //    followed by a DPP sum over the 16 lanes of the row; P.V takes two keys at a time as
 //    v_dot2_f32_bf16 of (p_i, p_i+1) with (v_i, v_i+1), 8 output dims per lane, and the row
 //    sum adds the same bf16 probabilities. When a chunk lies inside one block, one table
-//    lookup gives a scalar base and each lane adds a fixed offset. The 8B shape (G = 4) is
-//    instruction-bound, so these cuts matter as long as the kernel keeps 3 waves per SIMD.
+//    lookup gives a scalar base and each lane adds a fixed offset. The 8B shape (G = 4) was
+//    instruction-bound before these cuts (now about 360 VALU instructions per 16-key chunk,
+//    the VALU busy half the time); they pay as long as the kernel keeps 3 waves per SIMD.
 //    (Scores by a 16x16x32 bf16 MFMA with the query heads as columns were measured slower:
 //    the extra registers halve the waves per SIMD.)
 //  - The running max may lag by a bounded slack, so the output rescale is rare.

@@ -128,11 +128,31 @@ def cpu_baseline(shape, ds, k_cache, v_cache, scale, min_seconds: float = 10.0):
         if dt >= min_seconds or reps >= 200:
             break
     nbytes = decode_bytes(shape, m["context_lens"])
+    cores = oracle.num_threads()
+    # One core on a bounded sample: the step's first 32 sequences, about 5 s.
+    n1 = min(32, len(m["context_lens"]))
+    cl1, bt1 = m["context_lens"][:n1], m["block_tables"][:n1]
+    oracle.set_num_threads(1)
+    try:
+        reps1, t1 = 0, time.perf_counter()
+        while True:
+            oracle.attn_decode(q[:n1], kb, vb, cl1, bt1, shape.num_heads, shape.num_kv_heads,
+                               shape.head_dim, shape.block_size, scale)
+            reps1 += 1
+            dt1 = time.perf_counter() - t1
+            if dt1 >= min_seconds / 2 or reps1 >= 200:
+                break
+    finally:
+        oracle.set_num_threads(cores)
+    nbytes1 = decode_bytes(shape, cl1)
     return {"value": round(reps * nbytes / dt / 1e9, 3), "unit": "GB/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
+            "cores": cores, "kind": "oracle",
             "sample": f"whole decode step ({len(m['context_lens'])} sequences, "
                       f"{nbytes / 1e9:.2f} GB of K/V) in fp64 C, {reps} repetitions in "
-                      f"{dt:.1f} s"}
+                      f"{dt:.1f} s",
+            "single_core_value": round(reps1 * nbytes1 / dt1 / 1e9, 3),
+            "single_core_sample": f"first {n1} sequences ({nbytes1 / 1e9:.2f} GB of K/V), "
+                                  f"{reps1} repetitions in {dt1:.1f} s on 1 thread"}
 
 
 def norm_rope_store_part(shape, dsteps, k_cache, v_cache, iters: int) -> dict:

@@ -110,6 +110,18 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, group: int) -> dict:
             "write_bytes_per_launch": round(write), "bytes_per_launch": round(fetch + write)}
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (first entry of /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(shape, ds, k_cache, v_cache, scale, min_seconds: float = 10.0):
     """The oracle (as it stands) on the host cores: the whole decode step of the workload."""
     import oracle  # test infrastructure: the baseline leg only
@@ -150,6 +162,7 @@ def cpu_baseline(shape, ds, k_cache, v_cache, scale, min_seconds: float = 10.0):
             "sample": f"whole decode step ({len(m['context_lens'])} sequences, "
                       f"{nbytes / 1e9:.2f} GB of K/V) in fp64 C, {reps} repetitions in "
                       f"{dt:.1f} s",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
             "single_core_value": round(reps1 * nbytes1 / dt1 / 1e9, 3),
             "single_core_sample": f"first {n1} sequences ({nbytes1 / 1e9:.2f} GB of K/V), "
                                   f"{reps1} repetitions in {dt1:.1f} s on 1 thread"}

@@ -412,8 +412,8 @@ def small_decode_latency(dev, iters: int, layers: int = 28) -> dict:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mixed_8b")
     ap.add_argument("--tp", type=int, default=1,
                     help="run one rank's share of a tensor-parallel deployment of degree TP "

@@ -366,7 +366,7 @@ def small_decode_latency(dev, iters: int, layers: int = 28) -> dict:
     vs = [vc] + [vc.clone() for _ in range(layers - 1)]
     assert t.key.shape[0] == t.q_decode.shape[0]  # decode-only step: one new row per sequence
     dg = graphs.DecodeGraphs(w.shape, ks, vs, max_bs=8, max_blocks=ds.decode_tables.shape[1],
-                             scale=scale)
+                             scale=scale, fused=False)
     dgf = graphs.DecodeGraphs(w.shape, ks, vs, max_bs=8, max_blocks=ds.decode_tables.shape[1],
                               scale=scale, fused=True)
     args = (t.q_decode, t.key, t.value, ds.slot_mapping, ds.context_lens, ds.decode_tables)

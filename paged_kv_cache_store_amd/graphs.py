@@ -11,8 +11,10 @@ pool or the real rows. Block-table rows are not cleared between steps: entries p
 own context are never read.
 
 The recorded launches are the library's kernels only (no memset nodes); padding values are
-written by ordinary eager fills before the replay. With ``fused=True`` each layer records one
-store+decode call (nv_paged_attn_decode_store) instead of the store and the decode.
+written by ordinary eager fills before the replay. By default (``fused=True``) each layer
+records one store+decode call (nv_paged_attn_decode_store, split rows merged in the same
+launch through arrival counters) instead of the store and the decode; ``fused=False``
+records the two calls. Both give the same bits.
 """
 from __future__ import annotations
 
@@ -38,7 +40,7 @@ class DecodeGraphs:
     the block size)."""
 
     def __init__(self, shape: AttnShape, k_cache, v_cache, max_bs: int, max_blocks: int,
-                 scale: float | None = None, fused: bool = False,
+                 scale: float | None = None, fused: bool = True,
                  merge_in_kernel: bool = True):
         if max_bs < 1 or max_blocks < 1:
             raise ValueError("max_bs and max_blocks must be positive")

@@ -85,7 +85,8 @@ def test_graph_replay_matches_eager_and_oracle(shape, fused):
     assert np.array_equal(bits(k_cache), k_host) and np.array_equal(bits(v_cache), v_host)
 
 
-def test_graph_over_layer_stack():
+@pytest.mark.parametrize("fused", [False, True], ids=["two_call", "fused"])
+def test_graph_over_layer_stack(fused):
     """Three layers, each with its own pool, in one graph: every layer stores the step's rows
     into its own pool and attends over it; replay equals eager bitwise, each layer's output
     equals a single-layer eager call on that layer's pool."""
@@ -98,7 +99,7 @@ def test_graph_over_layer_stack():
     D = shape.num_kv_heads * shape.head_dim
     ks = [torch.randn(40 * bsz, D, generator=gen).bfloat16().to(dev) for _ in range(L)]
     vs = [torch.randn(40 * bsz, D, generator=gen).bfloat16().to(dev) for _ in range(L)]
-    dg = graphs.DecodeGraphs(shape, ks, vs, max_bs=16, max_blocks=max_blocks)
+    dg = graphs.DecodeGraphs(shape, ks, vs, max_bs=16, max_blocks=max_blocks, fused=fused)
     seqs = _decode_batch(rng, pool, 6, 700, bsz)
     m = nvpaged.nv_prepare_decode(seqs, bsz)
     q = torch.randn(6, shape.num_heads, shape.head_dim, generator=gen).bfloat16().to(dev)

@@ -84,6 +84,13 @@ typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4v;
 // compiler's wait insertion does not treat the in-flight copy as aliasing every LDS read
 // (it would drain the copy before each one); completion is waited for explicitly
 // (s_waitcnt vmcnt) before the barrier that publishes a tile.
+//
+// M0 carries the LDS address of the copy. The compiler reports the m0 clobber as ignored (M0 is
+// a reserved register) but never uses M0 itself in these kernels: in their ISA every write of
+// M0 is one of these two helpers, each immediately followed by its copy. The clobber stays as
+// documentation and that one diagnostic is muted here.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void copy16_to_lds(const void *src, void *lds_base) {
     const uint32_t base = (uint32_t)(uintptr_t)lds_base;
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
@@ -102,6 +109,7 @@ __device__ __forceinline__ void copy16_to_lds_sbase(const void *sbase, uint32_t 
                  : "s"(__builtin_amdgcn_readfirstlane(base)), "v"(voff), "s"(sbase)
                  : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // Waits until at most N of this wave's memory loads are outstanding and all its LDS accesses
 // are done (loads complete in order, so the older tile's copies have landed), then meets the

@@ -113,6 +113,30 @@ def test_in_kernel_merge_stress():
     assert int(cnt.abs().sum()) == 0
 
 
+def test_fused_full_size_decode_large():
+    """The 0.6B decode of 256 sequences (contexts U[512, 4096], a 4608-block pool) at full size:
+    the one-launch call with arrival counters (two splits per long row, merged in the launch;
+    a large grid, so pairs are numbered sequence fastest) leaves the pools and the output equal,
+    bit for bit, to store then decode on a copy of the same pools."""
+    w = workloads.config_decode_large()
+    dev = torch.device("cuda")
+    kc, vc, tens = workloads.materialize(w, dev)
+    kc2, vc2 = kc.clone(), vc.clone()
+    scale = w.shape.head_dim ** -0.5
+    ds = gstep.prepare_step(w.shape, w.steps[0], tens[0], dev)
+    print(f"[decode_store full size] {w.name}", flush=True)
+    gstep.run_store(ds, kc, vc)
+    gstep.run_decode(ds, kc, vc, scale)
+    ref = ds.out_decode.clone()
+    ds.out_decode.fill_(float("nan"))
+    gstep.run_decode_store(ds, kc2, vc2, scale)
+    torch.cuda.synchronize()
+    assert torch.equal(ds.out_decode.view(torch.int16), ref.view(torch.int16))
+    assert torch.equal(kc.view(torch.int16), kc2.view(torch.int16))
+    assert torch.equal(vc.view(torch.int16), vc2.view(torch.int16))
+    assert int(ds.counters.abs().sum()) == 0
+
+
 def test_fused_unaligned_rows_fall_back():
     """A value view whose rows are not 16-byte aligned takes the two-call path, same result."""
     shape = workloads.AttnShape(8, 2, 128, 64)

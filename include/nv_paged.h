@@ -185,7 +185,10 @@ nv_status nv_qk_norm_rope_store(const void *qkv, int64_t qkv_row_stride,
  * key range of each sequence may be split into chunks processed in parallel; the partial
  * results (max, sum, weighted values) are then merged by a log-sum-exp combine. The split
  * length depends only on batch, num_kv_heads, max_blocks_per_seq and block_size; when no row
- * can span two splits the workspace size is 0 and a single kernel is launched.
+ * can span two splits a single attention kernel is launched. When the grid is too large to run
+ * in one go on the chip, a small kernel first orders the sequences longest first (by bucketed
+ * context length) into the workspace, and the attention kernel dispatches them in that order;
+ * the order changes no output. The workspace size is 0 only when neither applies.
  *
  *   q             device bf16 [batch, num_heads, head_dim] contiguous.
  *   context_lens  device int32 [batch], 0 <= context_lens[b] <= max_blocks_per_seq*block_size.

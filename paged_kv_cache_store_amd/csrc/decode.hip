@@ -129,6 +129,7 @@ struct DecodeArgs {
     int32_t n_pairs;  // batch * max_splits
     int32_t batch;
     int32_t splits_together;  // 1: a sequence's splits are consecutive pairs (small grids)
+    const int32_t *perm;      // large grids: sequences longest first (decode_order_kernel)
     int32_t xcd_heads;  // kv heads of one pair kept together on one XCD (divides num_kv_heads)
     float scale_log2;  // softmax_scale * log2(e)
     float rescale_slack;  // raw-score growth of a running max tolerated without a rescale
@@ -246,9 +247,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
     // (they start together, which matters when the last one merges). A larger grid numbers
     // sequences fastest: every sequence's first (longest) split is dispatched before any
     // second one, and each split index spreads over all XCDs.
+    // Large grids also take the sequences longest first (a permutation written just before),
+    // so the longest rows do not start last and leave a tail.
     const int pair = unit / per_pair;
-    const int b = a.splits_together ? pair / a.max_splits : pair % a.batch;
+    const int bi = a.splits_together ? pair / a.max_splits : pair % a.batch;
     const int s = a.splits_together ? pair % a.max_splits : pair / a.batch;
+    const int b = a.perm ? a.perm[bi] : bi;
 #elif NV_DECODE_HEAD_MAJOR
     const int g = blockIdx.x, s = blockIdx.y, b = blockIdx.z;
 #else
@@ -682,9 +686,49 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
     a.out[bh * kHeadDim + e] = __builtin_bit_cast(uint16_t, (__bf16)merge_splits(a, bh, nsplit, e));
 }
 
+// Sequences longest first, for the dispatch order of large decode grids: a counting sort of
+// context lengths into 1024 buckets (one workgroup, histogram and offsets in LDS). Rows of one
+// bucket land in any order; each row's result does not depend on the order.
+constexpr int kOrderThreads = 1024;
+__global__ __launch_bounds__(kOrderThreads) void decode_order_kernel(const int32_t *lens,
+                                                                     int32_t batch,
+                                                                     int64_t max_ctx,
+                                                                     int32_t *perm) {
+    __shared__ int32_t next[kOrderThreads];
+    __shared__ int32_t scan[kOrderThreads];
+    const int t = threadIdx.x;
+    auto key_of = [&](int32_t L) -> int {  // longer rows get smaller keys
+        const int64_t l = L < 0 ? 0 : (L > max_ctx ? max_ctx : L);
+        return kOrderThreads - 1 - (int)(l * kOrderThreads / (max_ctx + 1));
+    };
+    next[t] = 0;
+    __syncthreads();
+    for (int b = t; b < batch; b += kOrderThreads) atomicAdd(&next[key_of(lens[b])], 1);
+    __syncthreads();
+    const int count = next[t];
+    scan[t] = count;
+    __syncthreads();
+    for (int off = 1; off < kOrderThreads; off <<= 1) {  // inclusive prefix sum
+        const int x = t >= off ? scan[t - off] : 0;
+        __syncthreads();
+        scan[t] += x;
+        __syncthreads();
+    }
+    next[t] = scan[t] - count;  // first position of bucket t
+    __syncthreads();
+    for (int b = t; b < batch; b += kOrderThreads) perm[atomicAdd(&next[key_of(lens[b])], 1)] = b;
+}
+
 template <int G, bool kFused>
 nv_status launch_decode(const DecodeArgs &a, int batch, hipStream_t stream) {
 #if NV_DECODE_HEAD_MAJOR == 2
+    if (a.perm) {
+        const nv_status st = launch(decode_order_kernel, dim3(1), dim3(kOrderThreads), 0, stream,
+                                    a.context_lens, (int32_t)batch,
+                                    (int64_t)a.bt_width * a.block_size,
+                                    const_cast<int32_t *>(a.perm));
+        if (st != NV_OK) return st;
+    }
     const int64_t units = (int64_t)a.n_pairs * (a.num_kv_heads / a.xcd_heads);
     const dim3 grid((uint32_t)(8 * ((units + 7) / 8) * a.xcd_heads));
 #elif NV_DECODE_HEAD_MAJOR
@@ -702,13 +746,8 @@ int64_t max_context(int32_t max_blocks_per_seq, int32_t block_size) {
     return (int64_t)max_blocks_per_seq * block_size;
 }
 
-}  // namespace
-}  // namespace nvp
-
-extern "C" int32_t nv_paged_attn_decode_split_keys(int32_t batch, int32_t num_kv_heads,
-                                                   int32_t max_blocks_per_seq,
-                                                   int32_t block_size) {
-    using namespace nvp;
+int32_t split_keys_for(int32_t batch, int32_t num_kv_heads, int32_t max_blocks_per_seq,
+                       int32_t block_size) {
     // Largest split (fewest partials) that still yields enough work items over the padded
     // context, so every CU gets work; capped so that one split's table slice fits in LDS.
     const int64_t ctx = max_context(max_blocks_per_seq, block_size);
@@ -720,21 +759,60 @@ extern "C" int32_t nv_paged_attn_decode_split_keys(int32_t batch, int32_t num_kv
     return S;
 }
 
+// The launch shape and workspace layout of one decode call; the workspace size query and the
+// call itself both derive them here so they agree. Workspace: ml [B, Hq, splits, 2] (256-byte
+// padded), o [B, Hq, splits, head_dim], then the longest-first sequence order [B] (large grids
+// with more than one sequence only), 256-byte padded.
+struct DecodePlan {
+    int32_t split_keys = 0;
+    int64_t splits = 0;
+    int32_t xcd_heads = 1;
+    bool splits_together = true;
+    bool ordered = false;
+    size_t ml_bytes = 0, o_bytes = 0, perm_bytes = 0;
+    size_t total() const { return ml_bytes + o_bytes + perm_bytes; }
+};
+
+DecodePlan plan_decode(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t max_blocks_per_seq, int32_t block_size) {
+    DecodePlan p;
+    p.split_keys = split_keys_for(batch, num_kv_heads, max_blocks_per_seq, block_size);
+    p.splits = (max_context(max_blocks_per_seq, block_size) + p.split_keys - 1) / p.split_keys;
+    p.xcd_heads = std::gcd(num_kv_heads, NV_DECODE_XCD_HEADS > 0 ? (int32_t)NV_DECODE_XCD_HEADS
+                                                                  : num_heads / num_kv_heads);
+    // Workgroups of the 1D grid; up to 3 per CU (the register budget of G <= 4) it runs in one
+    // go on the 256 CUs. Larger grids run in waves, where the dispatch order matters.
+    const int64_t units = (int64_t)batch * p.splits * (num_kv_heads / p.xcd_heads);
+    p.splits_together = 8 * ((units + 7) / 8) * p.xcd_heads <= NV_DECODE_ONE_GO_GROUPS;
+    p.ordered = !p.splits_together && batch > 1;
+    if (p.splits > 1) {
+        const size_t rows = (size_t)batch * num_heads * p.splits;
+        p.ml_bytes = (rows * 2 * sizeof(float) + 255) / 256 * 256;
+        p.o_bytes = (rows * head_dim * sizeof(float) + 255) / 256 * 256;
+    }
+    if (p.ordered) p.perm_bytes = ((size_t)batch * sizeof(int32_t) + 255) / 256 * 256;
+    return p;
+}
+
+}  // namespace
+}  // namespace nvp
+
+extern "C" int32_t nv_paged_attn_decode_split_keys(int32_t batch, int32_t num_kv_heads,
+                                                   int32_t max_blocks_per_seq,
+                                                   int32_t block_size) {
+    return nvp::split_keys_for(batch, num_kv_heads, max_blocks_per_seq, block_size);
+}
+
 extern "C" size_t nv_paged_attn_decode_workspace_size(int32_t batch, int32_t num_heads,
                                                       int32_t num_kv_heads, int32_t head_dim,
                                                       int32_t max_blocks_per_seq,
                                                       int32_t block_size) {
-    using namespace nvp;
     if (batch <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
-        max_blocks_per_seq <= 0 || block_size <= 0)
+        max_blocks_per_seq <= 0 || block_size <= 0 || num_heads % num_kv_heads != 0)
         return 0;
-    const int32_t S = nv_paged_attn_decode_split_keys(batch, num_kv_heads, max_blocks_per_seq,
-                                                      block_size);
-    const int64_t splits = (max_context(max_blocks_per_seq, block_size) + S - 1) / S;
-    if (splits <= 1) return 0;
-    const size_t rows = (size_t)batch * num_heads * splits;
-    const size_t ml = (rows * 2 * sizeof(float) + 255) / 256 * 256;
-    return ml + rows * head_dim * sizeof(float);
+    return nvp::plan_decode(batch, num_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                            block_size)
+        .total();
 }
 
 namespace nvp {
@@ -846,9 +924,9 @@ nv_status decode_impl(const void *q, const void *k_cache, const void *v_cache,
         return launch(decode_combine_kernel, dim3(num_heads, batch), dim3(kHeadDim), 0, stream, z);
     }
     if (!block_tables) return NV_ERR_INVALID_ARG;
-    const size_t need = nv_paged_attn_decode_workspace_size(batch, num_heads, num_kv_heads,
-                                                            head_dim, max_blocks_per_seq,
-                                                            block_size);
+    const DecodePlan p = plan_decode(batch, num_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                                     block_size);
+    const size_t need = p.total();
     if (need > 0 && (!workspace || workspace_bytes < need ||
                      reinterpret_cast<uintptr_t>(workspace) % 256 != 0))
         return NV_ERR_WORKSPACE;
@@ -864,29 +942,19 @@ nv_status decode_impl(const void *q, const void *k_cache, const void *v_cache,
     a.num_kv_heads = num_kv_heads;
     a.block_size = block_size;
     a.bs_shift = (block_size & (block_size - 1)) == 0 ? __builtin_ctz((unsigned)block_size) : -1;
-    a.split_keys = nv_paged_attn_decode_split_keys(batch, num_kv_heads, max_blocks_per_seq,
-                                                   block_size);
-    const int64_t splits = (max_context(max_blocks_per_seq, block_size) + a.split_keys - 1) /
-                           a.split_keys;
-    if (splits > 65535) return NV_ERR_UNSUPPORTED;
-    a.max_splits = (int32_t)splits;
-    if ((int64_t)batch * splits * num_kv_heads + 8 * (int64_t)num_kv_heads > INT32_MAX)
+    a.split_keys = p.split_keys;
+    if (p.splits > 65535) return NV_ERR_UNSUPPORTED;
+    a.max_splits = (int32_t)p.splits;
+    if ((int64_t)batch * p.splits * num_kv_heads + 8 * (int64_t)num_kv_heads > INT32_MAX)
         return NV_ERR_UNSUPPORTED;  // grid size
-    a.n_pairs = (int32_t)(batch * splits);
+    a.n_pairs = (int32_t)(batch * p.splits);
     a.batch = batch;
-    a.xcd_heads = std::gcd(num_kv_heads, NV_DECODE_XCD_HEADS > 0 ? (int32_t)NV_DECODE_XCD_HEADS
-                                                                  : num_heads / num_kv_heads);
-    {
-        // Workgroups of the 1D grid; up to 3 per CU (the register budget of G <= 4) it runs
-        // in one go on the 256 CUs.
-        const int64_t units = (int64_t)a.n_pairs * (num_kv_heads / a.xcd_heads);
-        a.splits_together = 8 * ((units + 7) / 8) * a.xcd_heads <= NV_DECODE_ONE_GO_GROUPS;
-    }
-    const size_t rows = (size_t)batch * num_heads * splits;
-    const size_t ml_bytes = (rows * 2 * sizeof(float) + 255) / 256 * 256;
-    a.ws_ml = need ? static_cast<float *>(workspace) : nullptr;
-    a.ws_o = need ? reinterpret_cast<float *>(static_cast<char *>(workspace) + ml_bytes)
-                  : nullptr;
+    a.xcd_heads = p.xcd_heads;
+    a.splits_together = p.splits_together;
+    char *ws = static_cast<char *>(workspace);
+    a.ws_ml = p.ml_bytes ? reinterpret_cast<float *>(ws) : nullptr;
+    a.ws_o = p.o_bytes ? reinterpret_cast<float *>(ws + p.ml_bytes) : nullptr;
+    a.perm = p.ordered ? reinterpret_cast<int32_t *>(ws + p.ml_bytes + p.o_bytes) : nullptr;
     a.scale_log2 = softmax_scale * kLog2e;
     a.rescale_slack = NV_DECODE_SLACK / a.scale_log2;
     a.new_k = fs ? fs->key : nullptr;

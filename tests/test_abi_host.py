@@ -206,7 +206,9 @@ def test_decode_split_choice(nv):
     assert nv.nv_paged_attn_decode_split_keys(256, 8, 16, 256) == 2048  # 2048 pairs x 2
     assert nv.nv_paged_attn_decode_split_keys(512, 8, 16, 256) == 8192
     assert nv.nv_paged_attn_decode_split_keys(64, 8, 16, 256) == 512  # 512 pairs x 8 splits
-    assert nv.nv_paged_attn_decode_workspace_size(512, 32, 8, 128, 16, 256) == 0
+    # Unsplit, but a grid that runs in waves: the workspace holds only the longest-first
+    # sequence order, one int32 per sequence, padded to 256 bytes.
+    assert nv.nv_paged_attn_decode_workspace_size(512, 32, 8, 128, 16, 256) == 2048
     prev = None
     for b in (1, 3, 17, 100, 600, 5000):
         s = nv.nv_paged_attn_decode_split_keys(b, 8, 16, 256)
@@ -215,8 +217,13 @@ def test_decode_split_choice(nv):
         prev = s
     # Tiny blocks cap the split so one split's table slice fits the kernel's staging area.
     assert nv.nv_paged_attn_decode_split_keys(4, 8, 4096, 1) <= 262
-    # One split covers every context: no workspace needed.
-    assert nv.nv_paged_attn_decode_workspace_size(4096, 16, 8, 128, 1, 256) == 0
+    # One split over a grid that fits the chip in one go: no workspace needed.
+    assert nv.nv_paged_attn_decode_workspace_size(4, 16, 8, 128, 1, 128) == 0
+    assert nv.nv_paged_attn_decode_workspace_size(4096, 16, 8, 128, 1, 256) == 16384
+    # A split grid adds the order after the partial results.
+    n = 64 * 16 * 8  # 64 sequences x 16 heads x 8 splits of 512 keys
+    assert nv.nv_paged_attn_decode_workspace_size(64, 16, 8, 128, 16, 256) == (
+        n * 2 * 4 + n * 128 * 4 + 256)
 
 
 def test_tp_share_divides_heads_only():

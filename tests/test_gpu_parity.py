@@ -202,3 +202,34 @@ def test_tp_rank_shapes(tp, base):
     w = workloads.tp_share(w, tp)
     assert w.shape.num_heads == shape.num_heads // tp
     print(_full_check(w, f"{base} tp={tp}"))
+
+
+def test_large_grid_order_is_longest_first_permutation():
+    """A decode grid too large for one go orders its sequences longest first into the tail of
+    the workspace: a permutation of the rows whose bucketed lengths never increase. The rows'
+    outputs are still checked against the oracle (the order changes none of them)."""
+    from paged_kv_cache_store_amd import nvpaged, step as gstep
+    shape = workloads.AttnShape(16, 8, 128, 16)
+    w = workloads.random_workload(47, shape, 0, 700, max_len=2000, pad_rows=12)
+    run = Run(w)
+    ds = gstep.prepare_step(shape, w.steps[0], run.tensors[0], "cuda")
+    B, width = ds.decode_tables.shape
+    need = nvpaged.nv_paged_attn_decode_workspace_size(B, 16, 8, 128, width, 16)
+    S = nvpaged.nv_paged_attn_decode_split_keys(B, 8, width, 16)
+    splits = -(-width * 16 // S)
+    rows = B * 16 * splits
+    part = 0 if splits == 1 else -(-rows * 8 // 256) * 256 + -(-rows * 512 // 256) * 256
+    assert need == part + -(-B * 4 // 256) * 256
+    ds.workspace.fill_(0xFF)
+    print(f"[order] {B} rows, {splits} splits, table width {width}", flush=True)
+    gstep.run_step(ds, run.k_cache, run.v_cache, run.scale)
+    torch.cuda.synchronize()
+    perm = ds.workspace[part:part + 4 * B].view(torch.int32).cpu().numpy()
+    assert sorted(perm.tolist()) == list(range(B))
+    lens = ds.context_lens.cpu().numpy().astype(np.int64)
+    max_ctx = width * 16
+    bucket = np.clip(lens, 0, max_ctx) * 1024 // (max_ctx + 1)
+    assert (np.diff(bucket[perm]) <= 0).all()
+    run.oracle_store(0)
+    ids, ref = run.oracle_decode(0, list(range(0, 700, 9)))
+    print(assert_attn_close(ds.out_decode[ids], ref, "ordered decode"))

@@ -64,7 +64,7 @@ CALIB_ELEMS = 1 << 28  # int32 elements of the counter-calibration op (1 GiB rea
 
 
 def load_traffic():
-    """HBM bytes per decode call (split + combine kernels) from the committed counter summary,
+    """HBM bytes per decode call (order, split and combine kernels) from the committed counter summary,
     if it was taken on the current kernel source; otherwise None."""
     if not os.path.exists(TRAFFIC_JSON):
         return None
@@ -94,7 +94,8 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, group: int) -> dict:
             name = r["Kernel_Name"]
             key = ("calib" if "bitwise_not" in name else
                    "split" if f"decode_split_kernel<{group}, false>" in name else
-                   "combine" if "decode_combine_kernel" in name else None)
+                   "combine" if "decode_combine_kernel" in name else
+                   "order" if "decode_order_kernel" in name else None)
             if key:
                 vals.setdefault(key, []).append(float(r["Counter_Value"]) * 1024.0)
         return {k: statistics.median(v) for k, v in vals.items()}
@@ -103,8 +104,8 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, group: int) -> dict:
     w = per_kernel(write_csv, "WRITE_SIZE")
     true_bytes = 4.0 * CALIB_ELEMS
     ff, wf = true_bytes / f["calib"], true_bytes / w["calib"]
-    fetch = ff * (f["split"] + f.get("combine", 0.0))
-    write = wf * (w["split"] + w.get("combine", 0.0))
+    fetch = ff * (f["split"] + f.get("combine", 0.0) + f.get("order", 0.0))
+    write = wf * (w["split"] + w.get("combine", 0.0) + w.get("order", 0.0))
     return {"source_sha256_16": source_hash(DECODE_SRC), "fetch_factor": round(ff, 4),
             "write_factor": round(wf, 4), "fetch_bytes_per_launch": round(fetch),
             "write_bytes_per_launch": round(write), "bytes_per_launch": round(fetch + write)}
@@ -556,7 +557,7 @@ def main():
                        "frac_hbm_peak": round(dec_gbs / HBM_PEAK_GBS, 4), "bytes": dec_bytes,
                        **percentiles(per_step["decode"])},
         },
-        "roofline": {"bound": "hbm", "kernel": "decode (split kernel, + merge kernel when a row is split)",
+        "roofline": {"bound": "hbm", "kernel": "decode (order kernel + split kernel, + merge kernel when a row is split)",
                      "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
         "cpu_baseline": None,

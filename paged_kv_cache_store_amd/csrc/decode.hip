@@ -49,7 +49,10 @@
 //    first split is dispatched before any second one, and each split index spreads over all
 //    XCDs: numbered split fastest, the first splits sat on a fixed half of the XCDs), and
 //    split fastest when it runs in one go (a sequence's splits start together, which the
-//    in-kernel merge of small steps prefers).
+//    in-kernel merge of small steps prefers). Larger grids also take the sequences longest
+//    first, from a counting sort of the context lengths written just before the launch: the
+//    long rows start in the first wave of workgroups instead of leaving a tail (+3.5-6% on
+//    the 8B, 0.6B and tensor-parallel share decodes).
 //  - One-launch store + decode (nv_paged_attn_decode_store, a decode step's two calls): the
 //    workgroup holding a row's new token loads that key's row from the step's new K/V rows and
 //    writes it to the pools; with arrival counters the last workgroup of a split row to finish

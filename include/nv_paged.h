@@ -141,7 +141,8 @@ nv_status nv_attn_prefill_packed(const void *q, const void *k, int64_t k_row_str
 /* ------------------------------------------------------------------------------------------
  * Fused per-head QK RMSNorm + rotary embedding + K/V store ("Nano-vLLM Field Guide", Step 9.5,
  * Qwen3Attention.forward: q_norm / k_norm on every head, rotary_emb on q and k at the token's
- * position, then store_kvcache; layernorm.py and rotary_embedding.py for the formulas).
+ * position, then store_kvcache; the formulas are Step 10.4, layernorm.py, and Step 10.5,
+ * rotary_embedding.py).
  *
  * For token t, with its row of the fused projection output qkv[t] = [Hq q heads | Hkv k heads
  * | Hkv v heads] of head_dim values each:
@@ -164,8 +165,10 @@ nv_status nv_attn_prefill_packed(const void *q, const void *k, int64_t k_row_str
  *   q_out          device bf16 [num_tokens, Hq, head_dim] contiguous.
  *   k_out          device bf16 [num_tokens, Hkv, head_dim] contiguous, or NULL.
  *   k_cache/v_cache/slot_mapping/num_slots  as for nv_store_kvcache.
+ * Alignment: qkv, both norm weights, cos_sin_cache, q_out, k_out (when given), k_cache and
+ * v_cache must start on a 16-byte boundary (the kernel moves 16-byte vectors).
  * Supported: head_dim == 128, Hq % Hkv == 0. Errors: NV_ERR_INVALID_ARG (null pointer, bad
- * sizes, stride or eps), NV_ERR_UNSUPPORTED (head_dim), NV_ERR_LAUNCH.
+ * sizes, stride, eps or a misaligned buffer), NV_ERR_UNSUPPORTED (head_dim), NV_ERR_LAUNCH.
  * ------------------------------------------------------------------------------------------ */
 nv_status nv_qk_norm_rope_store(const void *qkv, int64_t qkv_row_stride,
                                 const int64_t *positions, const void *q_norm_weight,

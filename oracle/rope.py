@@ -4,8 +4,8 @@ Test infrastructure (like the rest of oracle/): only tests/, smoke() and the CPU
 of bench.py use it; the HIP path never does.
 
 What is computed ("Nano-vLLM Field Guide", Step 9.5, Qwen3Attention.forward: q_norm and k_norm
-on every head, then rotary_emb on q and k, then the store; layernorm.py for RMSNorm;
-rotary_embedding.py for the table and the rotation):
+on every head, then rotary_emb on q and k, then the store; Step 10.4, layernorm.py, for
+RMSNorm; Step 10.5, rotary_embedding.py, for the table and the rotation):
 
   RMSNorm of one head x (d values):  n = round_bf16(x / sqrt(mean(x^2) + eps)),
                                      y = round_bf16(n * w)   (w the bf16 weight of length d)

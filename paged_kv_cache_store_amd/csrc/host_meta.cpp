@@ -125,7 +125,8 @@ extern "C" nv_status nv_check_indices(const int32_t *slot_mapping, int64_t num_t
                                       const int32_t *lens, int32_t batch,
                                       int32_t max_blocks_per_seq, int32_t block_size,
                                       int64_t num_blocks, int64_t *bad_index) {
-    if (num_tokens < 0 || batch < 0 || block_size <= 0 || max_blocks_per_seq < 0)
+    if (num_tokens < 0 || num_slots < 0 || batch < 0 || block_size <= 0 ||
+        max_blocks_per_seq < 0 || num_blocks < 0)
         return NV_ERR_INVALID_ARG;
     if ((num_tokens > 0 && !slot_mapping) || (batch > 0 && (!block_tables || !lens)))
         return NV_ERR_INVALID_ARG;

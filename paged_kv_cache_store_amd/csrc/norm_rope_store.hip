@@ -2,8 +2,8 @@
 //
 // Operation ("Nano-vLLM Field Guide", Step 9.5, Qwen3Attention.forward: q_norm and k_norm on
 // every head of the fused projection output, rotary_emb on q and k at each token's position,
-// then store_kvcache; layernorm.py and rotary_embedding.py for the two formulas; Step 10.3 for
-// the store and its -1 slots):
+// then store_kvcache; Step 10.4, layernorm.py, and Step 10.5, rotary_embedding.py, for the two
+// formulas; Step 10.3 for the store and its -1 slots):
 //   RMSNorm of a head x (d = 128 values): n = bf16(x * rsqrt(mean(x^2) + eps)),
 //                                         y = bf16(n * w)
 //   rotary embedding, halves y1 = y[0:64], y2 = y[64:128], frequency i < 64 at position p:
@@ -158,6 +158,12 @@ extern "C" nv_status nv_qk_norm_rope_store(const void *qkv, int64_t qkv_row_stri
     if (num_tokens == 0) return NV_OK;
     if (!qkv || !positions || !q_norm_weight || !k_norm_weight || !cos_sin_cache || !q_out ||
         !k_cache || !v_cache || !slot_mapping)
+        return NV_ERR_INVALID_ARG;
+    // Every lane moves whole 16-byte vectors of these buffers (rows are 256-byte head slices,
+    // the table rows 512 bytes): their bases must be 16-byte aligned.
+    const auto a16 = [](const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+    if (!a16(qkv) || !a16(q_norm_weight) || !a16(k_norm_weight) || !a16(cos_sin_cache) ||
+        !a16(q_out) || (k_out && !a16(k_out)) || !a16(k_cache) || !a16(v_cache))
         return NV_ERR_INVALID_ARG;
     NormRopeArgs a;
     a.qkv = static_cast<const uint16_t *>(qkv);

@@ -192,7 +192,8 @@ def nv_attn_prefill_packed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
 def rope_cos_sin_cache(max_position: int, head_dim: int, base: float, device) -> torch.Tensor:
     """The engine's rotary table, fp32 [max_position, head_dim]: row p = cos(p theta_i) for
     i < head_dim/2, then sin(p theta_i), theta_i = base^(-2i/head_dim), computed in fp32 as the
-    engine does ("Nano-vLLM Field Guide", Step 9.5, rotary_embedding.py)."""
+    engine does ("Nano-vLLM Field Guide", Step 10.5, rotary_embedding.py). This init-time table
+    is an input of the fused call, like the norm weights, not a step of the hot path."""
     inv_freq = 1.0 / (base ** (torch.arange(0, head_dim, 2, dtype=torch.float) / head_dim))
     t = torch.arange(max_position, dtype=torch.float)
     freqs = torch.outer(t, inv_freq)

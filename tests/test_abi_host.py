@@ -120,6 +120,13 @@ def test_check_indices(nv):
     ok, bad = nv.nv_check_indices(np.zeros(0, np.int32), 8, np.array([[0, -1]], np.int32),
                                   np.array([5], np.int32), 4, 2)
     assert not ok and bad == 1  # padding entry inside the read range
+    # negative pool sizes are argument errors, reported before any slot is looked at
+    ok, bad = nv.nv_check_indices(np.array([3], np.int32), -1, np.zeros((0, 0), np.int32),
+                                  np.zeros(0, np.int32), 4, 2)
+    assert not ok and bad == -1
+    ok, bad = nv.nv_check_indices(np.array([3], np.int32), 8, np.array([[0]], np.int32),
+                                  np.array([2], np.int32), 4, -1)
+    assert not ok and bad == -1
 
 
 def test_device_calls_reject_bad_arguments_without_launch(nv):
@@ -257,6 +264,21 @@ def test_norm_rope_store_rejects_bad_arguments_without_launch(nv):
     assert L.nv_qk_norm_rope_store(*bad) == -1  # empty table
     bad = list(base); bad[2] = null
     assert L.nv_qk_norm_rope_store(*bad) == -1  # no positions
+
+
+def test_norm_rope_store_rejects_misaligned_buffers(nv):
+    """Every buffer the kernel moves in 16-byte vectors must be 16-byte aligned; a misaligned
+    one (e.g. a column-sliced qkv view) is an argument error, returned before any launch."""
+    L = nv.lib()
+    A = 1 << 20  # stand-in addresses: every call below fails before touching them
+    W = (16 + 2 * 8) * 128
+    base = [A, W, A, A, A, A, 4096, 1e-6, A, A, A, A, A, 4, 16, 8, 128, 64, None]
+    for i, name in ((0, "qkv"), (3, "q_norm_weight"), (4, "k_norm_weight"),
+                    (5, "cos_sin_cache"), (8, "q_out"), (9, "k_out"), (10, "k_cache"),
+                    (11, "v_cache")):
+        bad = list(base)
+        bad[i] = A + 8
+        assert L.nv_qk_norm_rope_store(*bad) == -1, name
 
 
 def test_rope_table_follows_the_formula():

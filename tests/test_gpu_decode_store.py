@@ -22,6 +22,8 @@ CASES = [  # shape, decode rows, max context, padding rows
     (workloads.QWEN3_8B, 9, 3000, 1),
     (workloads.AttnShape(12, 4, 128, 16), 7, 900, 2),
     (workloads.AttnShape(32, 4, 128, 48), 5, 700, 0),
+    (workloads.AttnShape(24, 4, 128, 256), 6, 2000, 1),   # G = 6
+    (workloads.AttnShape(12, 2, 128, 32), 11, 1200, 2),   # G = 6, block size 32
     (workloads.AttnShape(16, 8, 128, 256), 508, 1500, 4),  # 4096 pairs: unsplit, no merge
 ]
 

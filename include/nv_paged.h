@@ -49,7 +49,8 @@ typedef enum {
     NV_ERR_INVALID_ARG = -1, /* null pointer, negative size, inconsistent shapes or strides */
     NV_ERR_UNSUPPORTED = -2, /* valid request this build does not implement (e.g. head_dim) */
     NV_ERR_LAUNCH = -3,      /* the HIP runtime rejected a kernel launch */
-    NV_ERR_WORKSPACE = -4    /* decode workspace missing or smaller than required */
+    NV_ERR_WORKSPACE = -4,   /* decode workspace missing or smaller than required */
+    NV_ERR_SCRATCH = -5      /* the library's static scratch is smaller than the call needs */
 } nv_status;
 
 /* Static, human-readable name of a status code. Never NULL. */
@@ -220,6 +221,31 @@ nv_status nv_paged_attn_decode(const void *q, const void *k_cache, const void *v
                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                float softmax_scale, void *workspace, size_t workspace_bytes,
                                void *out, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Decode that allocates nothing, for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Same arguments as nv_paged_attn_decode without the workspace, and the same result bit for
+ * bit (the same kernels). The workspace is a static device array of NV_DECODE_SCRATCH_BYTES
+ * inside the library: each GPU the library runs on holds its own copy from the first call on
+ * that GPU until the process ends. The call allocates and frees nothing. Every call on one GPU
+ * shares that GPU's array and leaves garbage in it (no call needs it zeroed), so calls that
+ * overlap on one GPU (different streams or threads at the same time) race: issue them one
+ * after another, e.g. on one stream. The device is the current one; `stream` must belong to it.
+ * Errors: as nv_paged_attn_decode, and NV_ERR_SCRATCH, with nothing launched, when the call
+ * needs more than NV_DECODE_SCRATCH_BYTES of workspace (nv_paged_attn_decode_workspace_size()
+ * tells beforehand; e.g. batch 256 x 16 q heads over 4096-key contexts needs about 4 MiB).
+ * NV_ERR_LAUNCH also covers a failed lookup of the array's device address.
+ * ------------------------------------------------------------------------------------------ */
+#define NV_DECODE_SCRATCH_BYTES ((size_t)32 << 20)
+
+nv_status nv_paged_attn_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                       const int32_t *context_lens, const int32_t *block_tables,
+                                       int32_t max_blocks_per_seq, int32_t batch,
+                                       int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t block_size, float softmax_scale, void *out,
+                                       hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
  * Store + decode in one launch ("Nano-vLLM Field Guide", Step 10.3: store_kvcache, then

@@ -59,6 +59,8 @@
 //    merges the partials itself (coherent relaxed-atomic partials, no cache-wide fence), so
 //    neither a store kernel nor a merge kernel runs.
 // The split size depends only on host-known launch parameters: no device round trip.
+#include <atomic>
+#include <mutex>
 #include <numeric>
 
 #include "nv_common.h"
@@ -994,3 +996,66 @@ nv_status decode_impl(const void *q, const void *k_cache, const void *v_cache,
 
 }  // namespace
 }  // namespace nvp
+
+// ---- Decode without a caller workspace (callers that cannot allocate) ----
+//
+// The workspace of nv_paged_attn_decode_noalloc: one static device array; every GPU the
+// library runs on holds its own copy until the process ends. In host code `scratch` names a
+// host-side stand-in, not device memory: the device address comes from hipGetSymbolAddress,
+// once per device with that device current, and only that address reaches a kernel.
+static __device__ __align__(256) unsigned char scratch[NV_DECODE_SCRATCH_BYTES];
+
+namespace nvp {
+namespace {
+
+constexpr int kMaxScratchDevices = 256;
+std::atomic<void *> g_scratch_addr[kMaxScratchDevices];
+std::mutex g_scratch_lookup;
+
+// Device address of the current device's scratch array.
+nv_status device_scratch(void **addr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices)
+        return NV_ERR_LAUNCH;
+    void *p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_lookup);
+        p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+                return NV_ERR_LAUNCH;
+            g_scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *addr = p;
+    return NV_OK;
+}
+
+}  // namespace
+}  // namespace nvp
+
+extern "C" nv_status nv_paged_attn_decode_noalloc(const void *q, const void *k_cache,
+                                                  const void *v_cache,
+                                                  const int32_t *context_lens,
+                                                  const int32_t *block_tables,
+                                                  int32_t max_blocks_per_seq, int32_t batch,
+                                                  int32_t num_heads, int32_t num_kv_heads,
+                                                  int32_t head_dim, int32_t block_size,
+                                                  float softmax_scale, void *out,
+                                                  hipStream_t stream) {
+    using namespace nvp;
+    // The size is known on the host before anything runs (0 also for arguments the decode
+    // itself rejects); nothing is launched when it exceeds the array.
+    const size_t need = nv_paged_attn_decode_workspace_size(batch, num_heads, num_kv_heads,
+                                                            head_dim, max_blocks_per_seq,
+                                                            block_size);
+    if (need > NV_DECODE_SCRATCH_BYTES) return NV_ERR_SCRATCH;
+    void *ws = nullptr;
+    if (need > 0) {
+        const nv_status st = device_scratch(&ws);
+        if (st != NV_OK) return st;
+    }
+    return decode_impl(q, k_cache, v_cache, context_lens, block_tables, max_blocks_per_seq,
+                       batch, num_heads, num_kv_heads, head_dim, block_size, softmax_scale, ws,
+                       ws ? NV_DECODE_SCRATCH_BYTES : 0, out, stream, nullptr);
+}

@@ -14,6 +14,9 @@ extern "C" const char *nv_status_string(nv_status status) {
         case NV_ERR_UNSUPPORTED: return "NV_ERR_UNSUPPORTED: shape not implemented by this build";
         case NV_ERR_LAUNCH: return "NV_ERR_LAUNCH: kernel launch failed";
         case NV_ERR_WORKSPACE: return "NV_ERR_WORKSPACE: decode workspace missing or too small";
+        case NV_ERR_SCRATCH:
+            return "NV_ERR_SCRATCH: the call needs more workspace than the library's static "
+                   "scratch (NV_DECODE_SCRATCH_BYTES) holds";
     }
     return "unknown nv_status";
 }

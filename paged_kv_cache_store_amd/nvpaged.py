@@ -24,6 +24,7 @@ EXPORTS = ("nv_status_string", "nv_store_kvcache", "nv_paged_attn_prefill",
            "nv_attn_prefill_packed", "nv_qk_norm_rope_store",
            "nv_paged_attn_decode_workspace_size", "nv_paged_attn_decode",
            "nv_paged_attn_decode_split_keys", "nv_paged_attn_decode_store",
+           "nv_paged_attn_decode_noalloc",
            "nv_prepare_prefill", "nv_prepare_decode",
            "nv_check_indices", "nv_probe_stream_read")
 
@@ -54,6 +55,9 @@ def _bind(path: str) -> ctypes.CDLL:
     L.nv_paged_attn_decode.argtypes = [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
                                        _f32, _p, _sz, _p, _p]
     L.nv_paged_attn_decode.restype = ctypes.c_int
+    L.nv_paged_attn_decode_noalloc.argtypes = [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32,
+                                               _i32, _f32, _p, _p]
+    L.nv_paged_attn_decode_noalloc.restype = ctypes.c_int
     L.nv_paged_attn_decode_store.argtypes = [_p, _p, _i64, _p, _i64, _p, _p, _p, _i64, _p, _p,
                                              _i32, _i32, _i32, _i32, _i32, _i32, _f32, _p, _sz,
                                              _p, _i64, _p, _p]
@@ -72,7 +76,9 @@ def _bind(path: str) -> ctypes.CDLL:
 
 _lib = _bind(LIB_PATH)
 
-NV_OK, NV_ERR_INVALID_ARG, NV_ERR_UNSUPPORTED, NV_ERR_LAUNCH, NV_ERR_WORKSPACE = 0, -1, -2, -3, -4
+NV_OK, NV_ERR_INVALID_ARG, NV_ERR_UNSUPPORTED, NV_ERR_LAUNCH, NV_ERR_WORKSPACE, NV_ERR_SCRATCH = \
+    0, -1, -2, -3, -4, -5
+NV_DECODE_SCRATCH_BYTES = 32 << 20  # the static workspace of nv_paged_attn_decode_noalloc
 
 
 class NvError(RuntimeError):
@@ -328,6 +334,36 @@ def nv_paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
                                      int(block_size), float(softmax_scale), workspace.data_ptr(),
                                      workspace.numel() * workspace.element_size(), out.data_ptr(),
                                      _stream(stream)), "nv_paged_attn_decode")
+    return out
+
+
+def nv_paged_attn_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                 context_lens: torch.Tensor, block_tables: torch.Tensor,
+                                 num_kv_heads: int, block_size: int, softmax_scale: float,
+                                 out: torch.Tensor, stream=None) -> torch.Tensor:
+    """nv_paged_attn_decode with the library's static workspace: the C call allocates nothing
+    (and neither does this wrapper: ``out`` is the caller's). q, out [B, Hq, d] bf16."""
+    _dev(q, "q", torch.bfloat16)
+    if q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [batch, num_heads, head_dim] tensor")
+    b, hq, d = q.shape
+    _pool_rows(k_cache, "k_cache", num_kv_heads * d)
+    _pool_rows(v_cache, "v_cache", num_kv_heads * d)
+    _dev(context_lens, "context_lens", torch.int32)
+    _dev(block_tables, "block_tables", torch.int32)
+    if context_lens.numel() != b or not context_lens.is_contiguous():
+        raise ValueError("context_lens must have one entry per row")
+    if block_tables.dim() != 2 or block_tables.shape[0] != b or not block_tables.is_contiguous():
+        raise ValueError("block_tables must be a contiguous [batch, max_blocks] tensor")
+    _dev(out, "out", torch.bfloat16)
+    if out.shape != q.shape or not out.is_contiguous():
+        raise ValueError("out must be contiguous and shaped like q")
+    _check(_lib.nv_paged_attn_decode_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                             context_lens.data_ptr(), block_tables.data_ptr(),
+                                             block_tables.shape[1], b, hq, int(num_kv_heads), d,
+                                             int(block_size), float(softmax_scale),
+                                             out.data_ptr(), _stream(stream)),
+           "nv_paged_attn_decode_noalloc")
     return out
 
 

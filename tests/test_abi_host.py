@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(nv):
 
 
 def test_status_strings(nv):
-    for code in (0, -1, -2, -3, -4):
+    for code in (0, -1, -2, -3, -4, -5):
         assert nv.nv_status_string(code).startswith("NV_")
     assert nv.nv_status_string(7) == "unknown nv_status"
 
@@ -264,6 +264,17 @@ def test_norm_rope_store_rejects_bad_arguments_without_launch(nv):
     assert L.nv_qk_norm_rope_store(*bad) == -1  # empty table
     bad = list(base); bad[2] = null
     assert L.nv_qk_norm_rope_store(*bad) == -1  # no positions
+
+
+def test_noalloc_decode_rejects_oversize_without_launch(nv):
+    """The allocation-free decode refuses, before any device call, a request whose workspace
+    exceeds its static array (here 2048 rows x 64 q heads in 16 key splits: ~1 GiB)."""
+    L = nv.lib()
+    A = 1 << 20  # stand-in addresses: the call fails before touching them
+    need = nv.nv_paged_attn_decode_workspace_size(2048, 64, 8, 128, 4096, 1)
+    assert need > nv.NV_DECODE_SCRATCH_BYTES
+    assert L.nv_paged_attn_decode_noalloc(A, A, A, A, A, 4096, 2048, 64, 8, 128, 1, 0.088, A,
+                                          None) == nv.NV_ERR_SCRATCH
 
 
 def test_norm_rope_store_rejects_misaligned_buffers(nv):

@@ -259,21 +259,21 @@ def copy_ceiling(dev, nbytes: int = 1 << 30, reps: int = 10) -> dict:
 
 
 def read_ceiling(dev, nbytes: int = 4 << 30, reps: int = 10) -> dict:
-    """The library's streaming-read probe (nv_probe_stream_read) over `nbytes`, far larger
+    """The streaming-read probe (nv_probe_stream_read, libnvprobe.so) over `nbytes`, far larger
     than the caches: the HBM read rate a plain kernel reaches, the practical ceiling for the
     decode (read-only traffic). Median over `reps` HIP-event-timed calls."""
-    from paged_kv_cache_store_amd import nvpaged
+    from paged_kv_cache_store_amd import probe
     x = torch.ones(nbytes // 2, dtype=torch.bfloat16, device=dev)
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
     for _ in range(2):
-        nvpaged.nv_probe_stream_read(x, sink)
+        probe.nv_probe_stream_read(x, sink)
     torch.cuda.synchronize()
     ts = []
     for _ in range(reps):
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
-        nvpaged.nv_probe_stream_read(x, sink)
+        probe.nv_probe_stream_read(x, sink)
         b.record()
         torch.cuda.synchronize()
         ts.append(a.elapsed_time(b))

@@ -1,8 +1,9 @@
 /*
- * nv_probe.h - measurement helper of the same library (libnvpaged.so): not part of the paged-KV
- * path. It measures the HBM read rate that a plain streaming kernel reaches on this GPU, the
- * practical ceiling against which the bandwidth-bound kernels of the path (the decode, which
- * reads each K/V byte once) are compared beside the published peak.
+ * nv_probe.h - BENCHMARK-ONLY measurement helper, built into its own library (libnvprobe.so),
+ * not into the paged-KV library and not part of its path. It measures the HBM read rate that a
+ * plain streaming kernel reaches on this GPU, the practical ceiling against which the
+ * bandwidth-bound kernels of the path (the decode, which reads each K/V byte once) are compared
+ * beside the published peak. It includes nv_paged.h for the status type only.
  */
 #ifndef NV_PROBE_H
 #define NV_PROBE_H

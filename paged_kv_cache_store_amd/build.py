@@ -1,8 +1,9 @@
-"""Builds libnvpaged.so, the gfx950 HIP library behind include/nv_paged.h (and the measurement
-helper of include/nv_probe.h), in-tree.
+"""Builds, in-tree, libnvpaged.so, the gfx950 HIP library behind include/nv_paged.h, and
+libnvprobe.so, the benchmark's measurement helper behind include/nv_probe.h (not part of the
+paged-KV path).
 
 Every source is compiled for gfx950 only, with packed-fp32 instruction selection disabled, then
-linked into one shared library next to this file.
+linked into its shared library next to this file.
 """
 from __future__ import annotations
 
@@ -16,9 +17,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libnvpaged.so")
+PROBE_LIB_PATH = os.path.join(HERE, "libnvprobe.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["store.hip", "decode.hip", "prefill.hip", "norm_rope_store.hip", "probe_read.hip",
-           "host_meta.cpp"]
+SOURCES = ["store.hip", "decode.hip", "prefill.hip", "norm_rope_store.hip", "host_meta.cpp"]
+PROBE_SOURCES = ["probe_read.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC,
@@ -34,16 +36,22 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB_PATH + ".tmp"
+def _link(objs, path: str, verbose: bool) -> None:
+    tmp = path + ".tmp"
     subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp],
                    check=True)
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
     if verbose:
-        print("built", LIB_PATH)
+        print("built", path)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB_PATH, verbose)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB_PATH, verbose)
     return LIB_PATH
 
 

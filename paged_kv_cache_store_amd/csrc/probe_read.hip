@@ -1,5 +1,6 @@
-// Streaming-read probe (measurement only, not part of the paged-KV path): the HBM read rate a
-// plain kernel reaches, the practical ceiling for the decode, which reads each K/V byte once.
+// Streaming-read probe (benchmark-only measurement helper, built into libnvprobe.so, not part
+// of the paged-KV path): the HBM read rate a plain kernel reaches, the practical ceiling for
+// the decode, which reads each K/V byte once.
 //
 // Each lane reads 16-byte vectors with non-temporal loads in a grid-stride loop, eight loads in
 // flight per iteration, and folds them with XOR; the result is stored only if it equals an

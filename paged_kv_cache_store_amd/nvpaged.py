@@ -26,7 +26,7 @@ EXPORTS = ("nv_status_string", "nv_store_kvcache", "nv_paged_attn_prefill",
            "nv_paged_attn_decode_split_keys", "nv_paged_attn_decode_store",
            "nv_paged_attn_decode_noalloc",
            "nv_prepare_prefill", "nv_prepare_decode",
-           "nv_check_indices", "nv_probe_stream_read")
+           "nv_check_indices")
 
 _p, _i32, _i64, _f32, _sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
                               ctypes.c_size_t)
@@ -62,8 +62,6 @@ def _bind(path: str) -> ctypes.CDLL:
                                              _i32, _i32, _i32, _i32, _i32, _i32, _f32, _p, _sz,
                                              _p, _i64, _p, _p]
     L.nv_paged_attn_decode_store.restype = ctypes.c_int
-    L.nv_probe_stream_read.argtypes = [_p, _i64, _p, _p]
-    L.nv_probe_stream_read.restype = ctypes.c_int
     L.nv_prepare_prefill.argtypes = [_p, _p, _p, _p, _i32, _i32, _p, _p, _p, _p, _p, _p, _i32,
                                      _p]
     L.nv_prepare_prefill.restype = ctypes.c_int
@@ -495,13 +493,3 @@ def nv_check_indices(slot_mapping: np.ndarray, num_slots: int, block_tables: np.
         _check(st, "nv_check_indices")
     return st == NV_OK, int(bad.value)
 
-
-def nv_probe_stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
-    """Reads every byte of the contiguous device tensor ``src`` once (the streaming-read
-    probe of include/nv_probe.h, a measurement helper); ``sink`` is a device int32 tensor of at
-    least one element that the probe may write. The caller times it."""
-    if not src.is_cuda or not src.is_contiguous():
-        raise ValueError("src must be a contiguous device tensor")
-    _dev(sink, "sink", torch.int32)
-    _check(_lib.nv_probe_stream_read(src.data_ptr(), src.numel() * src.element_size(),
-                                     sink.data_ptr(), _stream(stream)), "nv_probe_stream_read")

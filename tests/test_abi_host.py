@@ -23,14 +23,25 @@ def nv():
     return nvpaged
 
 
+def _declared(header_name):
+    header = open(os.path.join(ROOT, "include", header_name)).read()
+    return set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(nv_\w+)\s*\(", header, re.M))
+
+
 def test_exports_every_declared_symbol(nv):
-    inc = os.path.join(ROOT, "include")
-    header = "".join(open(os.path.join(inc, f)).read() for f in sorted(os.listdir(inc))
-                     if f.endswith(".h"))
-    declared = set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(nv_\w+)\s*\(", header, re.M))
+    """libnvpaged.so exports exactly what nv_paged.h declares; the benchmark's probe library
+    exports what nv_probe.h declares, and the path's library does not export it."""
+    from paged_kv_cache_store_amd import probe
+    assert sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h")) == \
+        ["nv_paged.h", "nv_probe.h"]
+    declared = _declared("nv_paged.h")
     assert declared == set(nv.EXPORTS)
     for name in declared:
         assert hasattr(nv.lib(), name), name
+    assert _declared("nv_probe.h") == set(probe.EXPORTS)
+    for name in probe.EXPORTS:
+        assert hasattr(probe.lib(), name), name
+        assert not hasattr(nv.lib(), name), name
 
 
 def test_status_strings(nv):
@@ -318,9 +329,10 @@ def test_token_positions_match_oracle(name):
         assert np.array_equal(gstep.token_positions(st), np.concatenate(parts))
 
 
-def test_probe_argument_errors(nv):
+def test_probe_argument_errors():
     """The streaming-read probe rejects bad arguments before launching anything."""
-    L = nv.lib()
+    from paged_kv_cache_store_amd import probe
+    L = probe.lib()
     assert L.nv_probe_stream_read(None, 1024, 64, None) == -1
     assert L.nv_probe_stream_read(64, 1024, None, None) == -1
     assert L.nv_probe_stream_read(64, 1000, 64, None) == -1   # not a multiple of 16

@@ -7,12 +7,15 @@ block size 256), 512 decode sequences with contexts uniform in 256..4096 plus a 
 before timing starts.
 
 Prints one JSON line. `value` is the decode attention's algorithmic HBM throughput (each
-visible K/V element once, plus q, out, tables and lengths) over its event-timed duration;
-prefill TFLOP/s and store GB/s are reported beside it, and the CPU oracle is timed on the host
-on the same step's decode (repeated for about 10 s). Extra parts, timed apart from the step:
-the fresh prompts through the packed (no block table) prefill, the fused QK-norm + rotary
-embedding + K/V store over the step's rows, and a small decode step through 28 layers launched
-eagerly vs replayed from HIP graphs.
+visible K/V element once, plus q, out, tables and lengths) over its average event-timed
+duration in the step loop; prefill TFLOP/s and store GB/s (at their median step) are reported
+beside it, and the CPU oracle is timed on the host on the same step's decode and prefill (all
+host threads and one thread, median of 3 runs each). Extra parts, timed apart from the step:
+all five configurations (0.6B decode of 4 + 2 rows, 0.6B varlen prefill, 0.6B prefix-cached +
+chunked prefill, 0.6B decode of 256 rows, and this step) call by call, >= 50 repetitions each,
+cold and warm for the three small ones; the fresh prompts through the packed (no block table)
+prefill; the fused QK-norm + rotary embedding + K/V store over the step's rows; a small decode
+step through 28 layers launched eagerly vs replayed from HIP graphs.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixed_8b] [--tp T]
 """
@@ -123,50 +126,85 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(shape, ds, k_cache, v_cache, scale, min_seconds: float = 10.0):
-    """The oracle (as it stands) on the host cores: the whole decode step of the workload."""
+def _median_of(n: int, fn) -> tuple:
+    """Median wall time (s) of n runs of fn() and the list of times."""
+    ts = []
+    for _ in range(n):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    return sorted(ts)[n // 2], ts
+
+
+def cpu_baseline(shape, ds, k_cache, v_cache, scale, runs: int = 3):
+    """The oracle (as it stands, fp64 C with OpenMP) on the host cores: the step's whole decode
+    and its whole prefill with every host thread, and a bounded sample of each on one thread;
+    each timed as the median of `runs` runs. Input generation is excluded; the oracle's gather
+    through the block table is included."""
     import oracle  # test infrastructure: the baseline leg only
     from oracle import meta
     kb = k_cache.view(torch.int16).cpu().numpy().view(np.uint16)
     vb = v_cache.view(torch.int16).cpu().numpy().view(np.uint16)
-    q = ds.tensors.q_decode.view(torch.int16).cpu().numpy().view(np.uint16)
+    qd = ds.tensors.q_decode.view(torch.int16).cpu().numpy().view(np.uint16)
     m = meta.prepare_decode(ds.step.decode, shape.block_size)
-    # The whole decode step, repeated until at least min_seconds of host time (about 10 s).
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.attn_decode(q, kb, vb, m["context_lens"], m["block_tables"], shape.num_heads,
-                           shape.num_kv_heads, shape.head_dim, shape.block_size, scale)
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds or reps >= 200:
-            break
-    nbytes = decode_bytes(shape, m["context_lens"])
     cores = oracle.num_threads()
-    # One core on a bounded sample: the step's first 32 sequences, about 5 s.
-    n1 = min(32, len(m["context_lens"]))
-    cl1, bt1 = m["context_lens"][:n1], m["block_tables"][:n1]
+
+    def dec(n):
+        return lambda: oracle.attn_decode(qd[:n], kb, vb, m["context_lens"][:n],
+                                          m["block_tables"][:n], shape.num_heads,
+                                          shape.num_kv_heads, shape.head_dim, shape.block_size,
+                                          scale)
+
+    B = len(m["context_lens"])
+    n1 = min(32, B)
+    t_all, _ = _median_of(runs, dec(B))
     oracle.set_num_threads(1)
     try:
-        reps1, t1 = 0, time.perf_counter()
-        while True:
-            oracle.attn_decode(q[:n1], kb, vb, cl1, bt1, shape.num_heads, shape.num_kv_heads,
-                               shape.head_dim, shape.block_size, scale)
-            reps1 += 1
-            dt1 = time.perf_counter() - t1
-            if dt1 >= min_seconds / 2 or reps1 >= 200:
-                break
+        t_one, _ = _median_of(runs, dec(n1))
     finally:
         oracle.set_num_threads(cores)
-    nbytes1 = decode_bytes(shape, cl1)
-    return {"value": round(reps * nbytes / dt / 1e9, 3), "unit": "GB/s",
-            "cores": cores, "kind": "oracle",
-            "sample": f"whole decode step ({len(m['context_lens'])} sequences, "
-                      f"{nbytes / 1e9:.2f} GB of K/V) in fp64 C, {reps} repetitions in "
-                      f"{dt:.1f} s",
-            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
-            "single_core_value": round(reps1 * nbytes1 / dt1 / 1e9, 3),
-            "single_core_sample": f"first {n1} sequences ({nbytes1 / 1e9:.2f} GB of K/V), "
-                                  f"{reps1} repetitions in {dt1:.1f} s on 1 thread"}
+    nbytes = decode_bytes(shape, m["context_lens"])
+    nbytes1 = decode_bytes(shape, m["context_lens"][:n1])
+    res = {"value": round(nbytes / t_all / 1e9, 3), "unit": "GB/s", "cores": cores,
+           "kind": "oracle",
+           "sample": f"whole decode step ({B} sequences, {nbytes / 1e9:.2f} GB of K/V) in fp64 "
+                     f"C, median of {runs} runs ({t_all:.2f} s each)",
+           "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+           "single_core_value": round(nbytes1 / t_one / 1e9, 3),
+           "single_core_sample": f"first {n1} sequences ({nbytes1 / 1e9:.2f} GB of K/V) on 1 "
+                                 f"thread, median of {runs} runs ({t_one:.2f} s each)"}
+    if ds.cu_seqlens_q is not None:
+        qp = ds.tensors.q_prefill.view(torch.int16).cpu().numpy().view(np.uint16)
+        pm = meta.prepare_prefill(ds.step.prefill, shape.block_size)
+        args = (shape.num_heads, shape.num_kv_heads, shape.head_dim, shape.block_size, scale)
+        flops = prefill_flops(shape, ds.step.prefill)
+        t_pre, _ = _median_of(runs, lambda: oracle.attn_prefill(
+            qp, kb, vb, pm["cu_seqlens_q"], pm["cu_seqlens_k"], pm["block_tables"], *args))
+        # one thread: the first 512 new rows of the first prompt (a prompt's leading rows see
+        # only keys up to their own position, as in the full prefill)
+        s0 = ds.step.prefill[0]
+        rows = min(512, s0.num_new)
+        from paged_kv_cache_store_amd.workloads import Seq
+        sub = [Seq(s0.block_table, s0.num_cached, rows)]
+        pm1 = meta.prepare_prefill(sub, shape.block_size)
+        flops1 = prefill_flops(shape, sub)
+        oracle.set_num_threads(1)
+        try:
+            t_pre1, _ = _median_of(runs, lambda: oracle.attn_prefill(
+                qp[:rows], kb, vb, pm1["cu_seqlens_q"], pm1["cu_seqlens_k"],
+                pm1["block_tables"], *args))
+        finally:
+            oracle.set_num_threads(cores)
+        res["prefill"] = {
+            "value": round(flops / t_pre / 1e9, 2), "unit": "GFLOP/s", "cores": cores,
+            "sample": f"whole prefill of the step ({len(ds.step.prefill)} prompts, "
+                      f"{flops / 1e9:.1f} GFLOP) in fp64 C, median of {runs} runs "
+                      f"({t_pre:.2f} s each)",
+            "single_core_value": round(flops1 / t_pre1 / 1e9, 3),
+            "single_core_sample": f"first {rows} rows of the first prompt ({flops1 / 1e9:.2f} "
+                                  f"GFLOP) on 1 thread, median of {runs} runs "
+                                  f"({t_pre1:.2f} s each)"}
+    return res
 
 
 def norm_rope_store_part(shape, dsteps, k_cache, v_cache, iters: int) -> dict:
@@ -410,6 +448,111 @@ def small_decode_latency(dev, iters: int, layers: int = 28) -> dict:
     return res
 
 
+FLUSH_BYTES = 512 << 20  # larger than L2 (4 MB per XCD) and the 256 MB MALL together
+
+
+def time_calls(fn, reps: int, flush=None, sleep_cycles: int = 1_000_000) -> list:
+    """Per-call HIP-event times (ms) of fn() over `reps` repetitions. Each repetition is queued
+    behind a GPU sleep kernel, so the host has launched everything before the timed call starts
+    and no launch gap falls inside it. Cold (flush given): the flush buffer is overwritten right
+    before the timed call, evicting L2 and MALL. Warm: the same call runs once, untimed, right
+    before the timed one."""
+    stream = torch.cuda.current_stream()
+    times = []
+    for _ in range(reps):
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(sleep_cycles)
+        if flush is not None:
+            flush.fill_(1)
+        else:
+            fn()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    return times
+
+
+def _rate(times_ms, work: int, kind: str) -> dict:
+    """Median / p10 / p90 of per-call times and the rate at the median against its peak."""
+    p = percentiles(times_ms)
+    t = p["ms_p50"] * 1e-3
+    if kind == "bytes":
+        r = work / t / 1e9
+        return {**p, "GB/s": round(r, 1), "frac_hbm_peak": round(r / HBM_PEAK_GBS, 4),
+                "bytes": work, "reps": len(times_ms)}
+    r = work / t / 1e12
+    return {**p, "TFLOP/s": round(r, 1), "frac_bf16_peak": round(r / BF16_PEAK_TFLOPS, 4),
+            "flops": work, "reps": len(times_ms)}
+
+
+def config_parts(dev, reps: int, mixed=None) -> dict:
+    """Every configuration's store, prefill and decode calls under one protocol: per-call HIP
+    events, `reps` repetitions, median / p10 / p90 and the rate at the median. The three small
+    configurations (which fit in the 256 MB MALL) are timed cold (L2 and MALL evicted by a
+    512 MiB write before each call) and warm (the same call just before); the two large ones
+    warm only (their K/V is far larger than the caches). A prefill configuration with two
+    steps reports each step and their sum. `mixed`: the 8B mixed step already resident (its
+    workload, pools and device steps)."""
+    from paged_kv_cache_store_amd import step as gstep
+    from paged_kv_cache_store_amd import workloads
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+    out = {}
+    for name in ("decode_small", "prefill_varlen", "prefix_chunked", "decode_large", "mixed_8b"):
+        if name == "mixed_8b" and mixed is not None:
+            w, k_cache, v_cache, dsteps = mixed
+        else:
+            w = workloads.CONFIGS[name]()
+            k_cache, v_cache, tens = workloads.materialize(w, dev, poison=False)
+            dsteps = [gstep.prepare_step(w.shape, st, t, dev) for st, t in zip(w.steps, tens)]
+        shape = w.shape
+        scale = shape.head_dim ** -0.5
+        cold_too = name in ("decode_small", "prefill_varlen", "prefix_chunked")
+        for ds in dsteps:  # every step's rows in the pool before any attention call
+            gstep.run_store(ds, k_cache, v_cache)
+        torch.cuda.synchronize()
+        rec = {"workload": w.name}
+        modes = ("cold", "warm") if cold_too else ("warm",)
+        for mode in modes:
+            fl = flush if mode == "cold" else None
+            parts = {}
+            pre_total, pre_flops = 0.0, 0
+            for i, (st, ds) in enumerate(zip(w.steps, dsteps)):
+                sfx = f"_step{i}" if len(dsteps) > 1 else ""
+                parts["store" + sfx] = _rate(
+                    time_calls(lambda: gstep.run_store(ds, k_cache, v_cache), reps, fl),
+                    store_bytes(shape, ds.host["slot_mapping"]), "bytes")
+                if st.prefill:
+                    f = prefill_flops(shape, st.prefill)
+                    r = _rate(time_calls(lambda: gstep.run_prefill(ds, k_cache, v_cache, scale),
+                                         reps, fl), f, "flops")
+                    parts["prefill" + sfx] = r
+                    pre_total += r["ms_p50"]
+                    pre_flops += f
+                if st.decode:
+                    parts["decode" + sfx] = _rate(
+                        time_calls(lambda: gstep.run_decode(ds, k_cache, v_cache, scale), reps,
+                                   fl), decode_bytes(shape, ds.host["decode"]["context_lens"]),
+                        "bytes")
+            if len(dsteps) > 1 and pre_flops:
+                tf = pre_flops / (pre_total * 1e-3) / 1e12
+                parts["prefill_all_steps"] = {"ms_p50_sum": round(pre_total, 4),
+                                              "TFLOP/s": round(tf, 1),
+                                              "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
+                                              "flops": pre_flops}
+            rec[mode] = parts
+        out[name] = rec
+        if name != "mixed_8b" or mixed is None:
+            del k_cache, v_cache, dsteps
+            torch.cuda.empty_cache()
+    del flush
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -525,9 +668,14 @@ def main():
         packed_ms = sum(a.elapsed_time(b) for a, b in pev) / args.steps
         packed_flops = sum(prefill_flops(shape, ds.step.prefill) for ds in packed)
 
+    # The headline and the roofline use the decode's average duration per step (the
+    # profiler's statistic); every part also reports its median step, at which store and
+    # prefill rates are given (a single slow step, e.g. the first one's launch gap, moves the
+    # mean of a 10 us call by far more than its median).
+    med = {n: percentiles(per_step[n])["ms_p50"] for n in names}
     dec_gbs = dec_bytes / (ms["decode"] * 1e-3) / 1e9 if dec_bytes else 0.0
-    pre_tflops = pre_flops / (ms["prefill"] * 1e-3) / 1e12 if pre_flops else 0.0
-    sto_gbs = sto_bytes / (ms["store"] * 1e-3) / 1e9
+    pre_tflops = pre_flops / (med["prefill"] * 1e-3) / 1e12 if pre_flops else 0.0
+    sto_gbs = sto_bytes / (med["store"] * 1e-3) / 1e9
     traffic = load_traffic()
 
     res = {
@@ -548,12 +696,16 @@ def main():
                    "block_size": shape.block_size, "decode_seqs": len(w.steps[0].decode),
                    "prefill_tokens": w.steps[0].num_prefill_tokens, "seed": w.seed},
         "parts": {
-            "store": {"ms": round(ms["store"], 4), "GB/s": round(sto_gbs, 1),
-                      "bytes": sto_bytes, **percentiles(per_step["store"])},
-            "prefill": {"ms": round(ms["prefill"], 4), "TFLOP/s": round(pre_tflops, 1),
+            "store": {"ms": round(med["store"], 4), "ms_mean": round(ms["store"], 4),
+                      "GB/s": round(sto_gbs, 1),
+                      "frac_hbm_peak": round(sto_gbs / HBM_PEAK_GBS, 4), "bytes": sto_bytes,
+                      **percentiles(per_step["store"])},
+            "prefill": {"ms": round(med["prefill"], 4), "ms_mean": round(ms["prefill"], 4),
+                        "TFLOP/s": round(pre_tflops, 1),
                         "frac_bf16_peak": round(pre_tflops / BF16_PEAK_TFLOPS, 4),
                         "flops": pre_flops, **percentiles(per_step["prefill"])},
-            "decode": {"ms": round(ms["decode"], 4), "GB/s": round(dec_gbs, 1),
+            "decode": {"ms": round(ms["decode"], 4), "ms_mean": round(ms["decode"], 4),
+                       "GB/s": round(dec_gbs, 1),
                        "frac_hbm_peak": round(dec_gbs / HBM_PEAK_GBS, 4), "bytes": dec_bytes,
                        **percentiles(per_step["decode"])},
         },
@@ -575,6 +727,9 @@ def main():
         res["roofline"]["measured_read_ceiling_GB/s"] = res["parts"]["read_ceiling"]["GB/s"]
         res["roofline"]["frac_of_measured_ceiling"] = round(
             dec_gbs / res["parts"]["read_ceiling"]["GB/s"], 4)
+    if not args.step_only and args.tp == 1 and args.workload == "mixed_8b":
+        res["parts"]["configs"] = config_parts(dev, max(50, args.steps),
+                                               mixed=(w, k_cache, v_cache, dsteps))
     if packed_ms:
         tf = packed_flops / (packed_ms * 1e-3) / 1e12
         res["parts"]["prefill_packed"] = {"ms": round(packed_ms, 4), "TFLOP/s": round(tf, 1),

@@ -131,6 +131,20 @@ __device__ __forceinline__ void wait_copies() {
     asm volatile("" ::: "memory");
 }
 
+// max / sum of x over lanes l and l ^ 32, in every lane: v_permlane32_swap trades the two
+// 32-lane halves of two registers in the VALU (a lane shuffle would go through LDS). With x in
+// both, the results hold [x(0..31), x(0..31)] and [x(32..63), x(32..63)].
+__device__ __forceinline__ float halves_max(float x) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
 // 16-byte chunk position of logical chunk c of tile row r in LDS.
 __device__ __forceinline__ int k_chunk_pos(int r, int c) { return c ^ (r & 15); }
 // V rows are read four at a time by 16-lane groups (32 bytes of each row) and two such groups
@@ -268,46 +282,59 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(NV_
         koff[j] = (uint32_t)(r * a.k_row_stride * 2) + 16 * k_chunk_pos(r, lane & 15);
         voff[j] = (uint32_t)(r * a.v_row_stride * 2) + 16 * v_chunk_pos(r, lane & 15);
     }
-    // Copies of one tile's K or V rows (wave w: rows kRowsPerWave w .. +kRowsPerWave) into dst.
-    auto copy_rows = [&](int key0, uint8_t *dst, const uint16_t *pool, const uint32_t *offs,
-                         bool is_v) {
-        const int64_t row_stride = is_v ? a.v_row_stride : a.k_row_stride;
-        if (NV_PREFILL_FASTCOPY && (packed || a.tile_in_block) && key0 + kTileKeys <= kv_end) {
-            int64_t row0;
-            if (packed) {
-                row0 = (int64_t)k_first + key0;
-            } else {
-                int lb, off0;
-                if (a.bs_shift >= 0) {
-                    lb = key0 >> a.bs_shift;
-                    off0 = key0 & (a.block_size - 1);
-                } else {
-                    lb = key0 / a.block_size;
-                    off0 = key0 - lb * a.block_size;
-                }
-                row0 = (int64_t)__builtin_amdgcn_readfirstlane(tbl[lb]) * a.block_size + off0;
-            }
-            const uint16_t *base = pool + row0 * row_stride + (int64_t)g * kHeadDim;
+    // Whole-block tiles (a multiple-of-64 block size, or packed rows) that end inside the keys
+    // take the fast copy: one block id per tile gives the tile's first pool row, and each lane
+    // adds its fixed offset. The block id comes from the LDS table one tile ahead (read while
+    // the current tile is computed), so the copy issue never waits on an LDS round trip; K and
+    // V share it.
+    auto fast_tile = [&](int key0) {
+        return NV_PREFILL_FASTCOPY && (packed || a.tile_in_block) && key0 + kTileKeys <= kv_end;
+    };
+    auto tile_block = [&](int key0) -> int {  // block id of a tile's first key (paged mode)
+        if (packed) return 0;
+        return tbl[a.bs_shift >= 0 ? key0 >> a.bs_shift : key0 / a.block_size];
+    };
+    auto copy_fast = [&](int64_t row0, uint8_t *dst, const uint16_t *pool, const uint32_t *offs,
+                         int64_t row_stride) {
+        const uint16_t *base = pool + row0 * row_stride + (int64_t)g * kHeadDim;
 #pragma unroll
-            for (int j = 0; j < kCopyGroups; ++j)
-                copy16_to_lds_sbase(base, offs[j], dst + (kRowsPerWave * w + 4 * j) * kRowBytes);
-            return;
-        }
+        for (int j = 0; j < kCopyGroups; ++j)
+            copy16_to_lds_sbase(base, offs[j], dst + (kRowsPerWave * w + 4 * j) * kRowBytes);
+    };
+    // Any other tile: each lane looks up its own key's row; keys past the end re-read the last
+    // valid key (masked later).
+    auto copy_rows = [&](int key0, uint8_t *dst, const uint16_t *pool, bool is_v) {
+        const int64_t row_stride = is_v ? a.v_row_stride : a.k_row_stride;
         const int pos = lane & 15;
 #pragma unroll
         for (int j = 0; j < kCopyGroups; ++j) {
             const int r = kRowsPerWave * w + 4 * j + (lane >> 4);
-            const int key = min(key0 + r, kv_end - 1);  // past the end: a valid row, masked later
+            const int key = min(key0 + r, kv_end - 1);
             const uint16_t *src = pool + key_row_staged(key) * row_stride + g * kHeadDim;
             const int c = is_v ? v_chunk_pos(r, pos) : k_chunk_pos(r, pos);
             copy16_to_lds(src + 8 * c, dst + (kRowsPerWave * w + 4 * j) * kRowBytes);
         }
     };
-    auto copy_k = [&](int t, int st) {
-        copy_rows(t * kTileKeys, k_lds[st], a.k_cache, koff, false);
-    };
-    auto copy_v = [&](int t, int st) {
-        copy_rows(t * kTileKeys, v_lds[st], a.v_cache, voff, true);
+    // K and V of tile t into stage st; blk: the tile's block id (fast tiles, paged mode).
+    auto copy_tile = [&](int t, int st, int blk) {
+        const int key0 = t * kTileKeys;
+        uint8_t *kd = k_lds[st];
+        uint8_t *vd = v_lds[st];
+        if (fast_tile(key0)) {
+            int64_t row0;
+            if (packed) {
+                row0 = (int64_t)k_first + key0;
+            } else {
+                const int off0 = a.bs_shift >= 0 ? (key0 & (a.block_size - 1))
+                                                 : key0 - (key0 / a.block_size) * a.block_size;
+                row0 = (int64_t)__builtin_amdgcn_readfirstlane(blk) * a.block_size + off0;
+            }
+            copy_fast(row0, kd, a.k_cache, koff, a.k_row_stride);
+            copy_fast(row0, vd, a.v_cache, voff, a.v_row_stride);
+            return;
+        }
+        copy_rows(key0, kd, a.k_cache, false);
+        copy_rows(key0, vd, a.v_cache, true);
     };
 
     // ---- S^T = K Q^T for the tile in LDS at Ks: two 32-key blocks ----
@@ -377,7 +404,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(NV_
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sc[kb][i]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        tmax = halves_max(tmax);
         // Rescale only when some row's max grew by more than the slack: until then the stale
         // max keeps every probability below 2^slack, far from fp32/bf16 overflow, and the
         // result is unchanged because the max cancels between O and l. The first tile always
@@ -440,21 +467,23 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(NV_
             for (int d = 0; d < 4; ++d)
                 o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[u][d], pb, o[d], 0, 0, 0);
         }
-        // Row sums of exactly the bf16 probabilities that multiplied V.
+        // Row sums of exactly the bf16 probabilities that multiplied V, in four independent
+        // chains (one dependent chain of 16 would expose its latency on every tile).
         const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-        float psum = 0.f;
+        float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-            psum = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pw[e]), ones, psum, false);
-        l_part += psum;
+            ps[e & 3] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pw[e]), ones, ps[e & 3], false);
+        l_part += (ps[0] + ps[1]) + (ps[2] + ps[3]);
     };
 
     f32x16 sc[2];
     // One tile per step: wait for its copies and publish it with a barrier (which also
     // retires the other stage), start copying the next tile into the other stage, then
-    // scores, softmax and P.V of this one.
-    copy_k(0, 0);
-    copy_v(0, 0);
+    // scores, softmax and P.V of this one. The block id of the tile after next is read from
+    // the LDS table during this step, so no copy waits on an LDS round trip.
+    copy_tile(0, 0, fast_tile(0) ? tile_block(0) : 0);
+    int blk_next = n_tiles > 1 && fast_tile(kTileKeys) ? tile_block(kTileKeys) : 0;
     // Q^T as the B operand: lane holds query row `col`, dims 16t + 8hg .. +8 for step t. The
     // query copies are this wave's oldest loads: wait until only the first tile's remain.
     wait_copies<2 * kCopyGroups>();
@@ -466,8 +495,9 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(NV_
         constexpr int st = decltype(stage)::value;
         wait_copies_and_barrier<0>();
         if (t + 1 < n_tiles) {
-            copy_k(t + 1, st ^ 1);
-            copy_v(t + 1, st ^ 1);
+            copy_tile(t + 1, st ^ 1, blk_next);
+            if (t + 2 < n_tiles && fast_tile((t + 2) * kTileKeys))
+                blk_next = tile_block((t + 2) * kTileKeys);
         }
         scores(k_lds[st], sc);
         bf16x8 vf0[4];
@@ -488,7 +518,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(NV_
     // v_permlane32_swap per word trades halves so that lane l ends with whole groups
     // 8 (2rp + 1) .. +7 and lane l + 32 with groups 8 (2rp) .. +7 (rp = 0, 1): 16-byte stores
     // instead of 8-byte ones.
-    const float l_tot = l_part + __shfl_xor(l_part, 32);
+    const float l_tot = halves_sum(l_part);
     const float inv = 1.f / l_tot;
     uint16_t *op = a.out + ((int64_t)(q0 + my_row) * a.num_heads + h) * kHeadDim;
 #pragma unroll

@@ -58,7 +58,14 @@ def store_bytes(shape, slot_mapping) -> int:
 
 
 def source_hash(path: str) -> str:
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    """Hash of a source's code: comments and whitespace are removed first, so a comment edit
+    does not invalidate counters taken on the same code."""
+    import re
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = " ".join(text.split())
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
 DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_store_amd", "csrc", "decode.hip")
@@ -352,6 +359,37 @@ def prefill_queued(dsteps, k_cache, v_cache, scale: float, flops: int, inner: in
     tf = flops / (us * 1e-6) / 1e12
     return {"us": round(us, 2), "TFLOP/s": round(tf, 1), "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
             "calls_per_region": inner}
+
+
+def prefill_context(dsteps, k_cache, v_cache, scale: float, flops: int, reps: int = 25) -> dict:
+    """The step's prefill calls timed one at a time (queued behind a sleep kernel, so no host
+    gap) after different predecessors: another prefill (its prompts' K/V and queries still in
+    L2 / MALL), the step's own order (decode of the previous step, then the store), and idle.
+    The kernel is the same; the difference is the cache state its first tiles meet."""
+    from paged_kv_cache_store_amd import step as gstep
+    pre = lambda: [gstep.run_prefill(ds, k_cache, v_cache, scale) for ds in dsteps]
+    dec = lambda: [gstep.run_decode(ds, k_cache, v_cache, scale) for ds in dsteps]
+    sto = lambda: [gstep.run_store(ds, k_cache, v_cache) for ds in dsteps]
+    ctxs = {"after_prefill": [pre], "after_decode_and_store": [dec, sto], "after_idle": []}
+    res = {k: [] for k in ctxs}
+    for _ in range(reps):
+        for name, before in ctxs.items():
+            if hasattr(torch.cuda, "_sleep"):
+                torch.cuda._sleep(2_000_000)
+            for f in before:
+                f()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            pre()
+            b.record()
+            torch.cuda.synchronize()
+            res[name].append(a.elapsed_time(b) * 1e3)
+    out = {}
+    for name, v in res.items():
+        us = sorted(v)[len(v) // 2]
+        out[name] = {"us": round(us, 2), "TFLOP/s": round(flops / (us * 1e-6) / 1e12, 1)}
+    return out
 
 
 def store_queued(dsteps, k_cache, v_cache, nbytes: int, inner: int = 20, reps: int = 5) -> dict:
@@ -722,6 +760,8 @@ def main():
         if pre_flops:
             res["parts"]["prefill_queued"] = prefill_queued(dsteps, k_cache, v_cache, scale,
                                                             pre_flops)
+            res["parts"]["prefill_context"] = prefill_context(dsteps, k_cache, v_cache, scale,
+                                                              pre_flops)
         res["parts"]["copy_ceiling"] = copy_ceiling(dev)
         res["parts"]["read_ceiling"] = read_ceiling(dev)
         res["roofline"]["measured_read_ceiling_GB/s"] = res["parts"]["read_ceiling"]["GB/s"]

@@ -659,6 +659,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
     // meets, and one lane counts the arrival; the workgroup that brings the count to nsplit
     // reads the partials with coherent loads, issued only after the count returned. Nothing
     // waits on another workgroup, so any dispatch order completes.
+    // Ordering, per the AMDGPU memory model's code sequences for gfx942-class targets (LLVM's
+    // AMDGPU backend user guide, "Memory Model GFX942"; the ISA here matches them): an
+    // agent-scope relaxed atomic store/load is a global store/load with sc1, performed at the
+    // device coherence point rather than in this XCD's L2; an agent-scope release is
+    // buffer_wbl2 sc1 + s_waitcnt vmcnt(0) and an acquire s_waitcnt vmcnt(0) + buffer_inv sc1,
+    // where the write-back and invalidate only serve non-atomic data. The partials are sc1
+    // atomics, so the wait below is the whole release they need: when the fetch_add is
+    // performed they are complete at the coherence point. The merger's sc1 loads depend on the
+    // fetch_add's result (barrier and branch), so they are issued after it returns and read
+    // the coherence point; no cache-wide write-back or invalidate is needed.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     uint32_t *cnt = a.counters + (int64_t)b * a.num_kv_heads + g;

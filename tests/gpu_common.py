@@ -18,17 +18,21 @@ ATOL_MEAN = 1e-3  # mean abs error bound vs the oracle
 
 
 def attn_bound(ref: np.ndarray) -> np.ndarray:
-    """Per-element bound: 1e-2, except where |ref| >= 4, where the bf16 output grid alone is
-    coarser than that; there the bound is half a bf16 ulp of the reference plus 2e-3."""
+    """Per-element bound: 1e-2 on the computed attention value, plus the conversion of that
+    value to the bf16 output ("Nano-vLLM Field Guide", Step 12.1: the output is in the model
+    dtype), which moves it by at most half a bf16 ulp of the result. The oracle is fp64 and
+    not rounded, so a result within 1e-2 before rounding can land up to 1e-2 + half an ulp
+    from it afterwards (half an ulp is 0.0039 for |o| in [1, 2), 0.0078 in [2, 4), 0.0156 in
+    [4, 8))."""
     mag = np.maximum(np.abs(ref), 1e-30)
     half_ulp = 0.5 * 2.0 ** (np.floor(np.log2(mag)) - 7)
-    return np.maximum(ATOL_MAX, half_ulp + 2e-3)
+    return ATOL_MAX + half_ulp
 
 
 def assert_attn_close(gpu: torch.Tensor, ref: np.ndarray, what: str) -> dict:
     """Checks the bound element by element and returns the error statistics, including how
-    many elements exceeded 1e-2 and were accepted only through the |ref| >= 4 rounding
-    allowance (``allowance_used``; each test prints it)."""
+    many elements exceeded 1e-2 and were accepted only through the output-rounding term
+    (``allowance_used``; each test prints it)."""
     g = gpu.detach().float().cpu().numpy().astype(np.float64)
     assert g.shape == ref.shape, (g.shape, ref.shape)
     assert np.isfinite(g).all(), f"{what}: non-finite output"

@@ -186,6 +186,16 @@ def test_device_calls_reject_bad_arguments_without_launch(nv):
                                   null) == 0  # empty batch
 
 
+def test_prefill_table_prefix_limit(nv):
+    """The block-table prefix a paged prefill stages in LDS holds 2048 entries: one more is
+    refused before anything is launched (stand-in addresses, never touched)."""
+    L = nv.lib()
+    A = 1 << 20
+    for bs in (1, 8, 256):
+        assert L.nv_paged_attn_prefill(A, A, A, A, A, 64, 2049 * bs, A, 2049, 1, 16, 8, 128, bs,
+                                       0.088, A, None) == nv.NV_ERR_UNSUPPORTED
+
+
 def test_decode_store_argument_errors(nv):
     """The one-launch store + decode rejects bad store arguments before launching anything."""
     L = nv.lib()

@@ -2,7 +2,7 @@
 
 K/V are read straight from packed [total_k, Hkv, d] tensors (V as a strided view into a fused
 QKV buffer, as the engine hands it over). Bounds as for the paged tests: max abs error <= 1e-2
-(half a bf16 ulp + 2e-3 where |o| >= 4), mean abs error <= 1e-3. The packed and paged paths
+plus half a bf16 ulp of the result, mean abs error <= 1e-3. The packed and paged paths
 perform the same arithmetic, so on the same keys their outputs must be bitwise equal.
 """
 import numpy as np

@@ -527,7 +527,46 @@ def _rate(times_ms, work: int, kind: str) -> dict:
             "flops": work, "reps": len(times_ms)}
 
 
-def config_parts(dev, reps: int, mixed=None) -> dict:
+def oracle_config(w, dsteps, k_cache, v_cache, runs: int = 3) -> dict:
+    """The oracle (fp64 C, all host threads) over one configuration's whole attention work: every
+    step's prefill and decode on host copies of the pools, median of `runs` runs; input copies
+    excluded, the oracle's gather through the tables included. Rates in the bench's units."""
+    import oracle  # test infrastructure: the CPU-baseline leg only
+    from oracle import meta
+    shape = w.shape
+    scale = shape.head_dim ** -0.5
+    kb = k_cache.view(torch.int16).cpu().numpy().view(np.uint16)
+    vb = v_cache.view(torch.int16).cpu().numpy().view(np.uint16)
+    args = (shape.num_heads, shape.num_kv_heads, shape.head_dim, shape.block_size, scale)
+    pre_calls, dec_calls, flops, nbytes = [], [], 0, 0
+    for st, ds in zip(w.steps, dsteps):
+        if st.prefill:
+            qp = ds.tensors.q_prefill.view(torch.int16).cpu().numpy().view(np.uint16)
+            pm = meta.prepare_prefill(st.prefill, shape.block_size)
+            pre_calls.append(lambda qp=qp, pm=pm: oracle.attn_prefill(
+                qp, kb, vb, pm["cu_seqlens_q"], pm["cu_seqlens_k"], pm["block_tables"], *args))
+            flops += prefill_flops(shape, st.prefill)
+        if st.decode:
+            qd = ds.tensors.q_decode.view(torch.int16).cpu().numpy().view(np.uint16)
+            dm = meta.prepare_decode(st.decode, shape.block_size)
+            bt = dm["block_tables"] if dm["block_tables"].shape[1] else \
+                np.full((len(st.decode), 1), -1, np.int32)
+            dec_calls.append(lambda qd=qd, dm=dm, bt=bt: oracle.attn_decode(
+                qd, kb, vb, dm["context_lens"], bt, *args))
+            nbytes += decode_bytes(shape, dm["context_lens"])
+    rec = {"cores": oracle.num_threads(), "runs": runs}
+    if pre_calls:
+        t, _ = _median_of(runs, lambda: [c() for c in pre_calls])
+        rec["prefill_s"] = round(t, 4)
+        rec["GFLOP/s"] = round(flops / t / 1e9, 2)
+    if dec_calls:
+        t, _ = _median_of(runs, lambda: [c() for c in dec_calls])
+        rec["decode_s"] = round(t, 4)
+        rec["GB/s"] = round(nbytes / t / 1e9, 3)
+    return rec
+
+
+def config_parts(dev, reps: int, mixed=None, with_oracle: bool = False) -> tuple:
     """Every configuration's store, prefill and decode calls under one protocol: per-call HIP
     events, `reps` repetitions, median / p10 / p90 and the rate at the median. The three small
     configurations (which fit in the 256 MB MALL) are timed cold (L2 and MALL evicted by a
@@ -538,7 +577,7 @@ def config_parts(dev, reps: int, mixed=None) -> dict:
     from paged_kv_cache_store_amd import step as gstep
     from paged_kv_cache_store_amd import workloads
     flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
-    out = {}
+    out, cpu = {}, {}
     for name in ("decode_small", "prefill_varlen", "prefix_chunked", "decode_large", "mixed_8b"):
         if name == "mixed_8b" and mixed is not None:
             w, k_cache, v_cache, dsteps = mixed
@@ -583,12 +622,14 @@ def config_parts(dev, reps: int, mixed=None) -> dict:
                                               "flops": pre_flops}
             rec[mode] = parts
         out[name] = rec
+        if with_oracle:
+            cpu[name] = oracle_config(w, dsteps, k_cache, v_cache)
         if name != "mixed_8b" or mixed is None:
             del k_cache, v_cache, dsteps
             torch.cuda.empty_cache()
     del flush
     torch.cuda.empty_cache()
-    return out
+    return out, cpu
 
 
 def main():
@@ -767,9 +808,11 @@ def main():
         res["roofline"]["measured_read_ceiling_GB/s"] = res["parts"]["read_ceiling"]["GB/s"]
         res["roofline"]["frac_of_measured_ceiling"] = round(
             dec_gbs / res["parts"]["read_ceiling"]["GB/s"], 4)
+    cpu_per_config = {}
     if not args.step_only and args.tp == 1 and args.workload == "mixed_8b":
-        res["parts"]["configs"] = config_parts(dev, max(50, args.steps),
-                                               mixed=(w, k_cache, v_cache, dsteps))
+        res["parts"]["configs"], cpu_per_config = config_parts(
+            dev, max(50, args.steps), mixed=(w, k_cache, v_cache, dsteps),
+            with_oracle=not args.no_cpu_baseline)
     if packed_ms:
         tf = packed_flops / (packed_ms * 1e-3) / 1e12
         res["parts"]["prefill_packed"] = {"ms": round(packed_ms, 4), "TFLOP/s": round(tf, 1),
@@ -777,6 +820,9 @@ def main():
                                           "flops": packed_flops}
     if not args.no_cpu_baseline and dsteps[0].context_lens is not None:
         res["cpu_baseline"] = cpu_baseline(shape, dsteps[0], k_cache, v_cache, scale)
+        if cpu_per_config:
+            # each configuration's whole attention work (every step's prefill and decode)
+            res["cpu_baseline"]["per_config"] = cpu_per_config
     print(json.dumps(res), flush=True)
 
 

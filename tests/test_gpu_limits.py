@@ -60,3 +60,34 @@ def test_prefill_full_table_prefix(bs):
     check_pools_bit_exact(run, "full table store")
     rows, ref = run.oracle_prefill(0, om)
     print(assert_attn_close(ds.out_prefill[rows], ref, f"full table prefix bs{bs}"))
+
+
+def test_empty_inputs_change_nothing():
+    """Every entry point called with nothing to do (no tokens, no sequences) returns success
+    and leaves its outputs and the pools untouched."""
+    dev = torch.device("cuda")
+    shape = workloads.QWEN3_0_6B
+    D = shape.row_elems
+    k = torch.randn(64, D, device=dev).bfloat16()
+    v = torch.randn(64, D, device=dev).bfloat16()
+    k0, v0 = bits(k).copy(), bits(v).copy()
+    key = torch.empty(0, shape.num_kv_heads, shape.head_dim, dtype=torch.bfloat16, device=dev)
+    slots = torch.empty(0, dtype=torch.int32, device=dev)
+    nvpaged.nv_store_kvcache(key, key, k, v, slots)
+    q = torch.empty(0, shape.num_heads, shape.head_dim, dtype=torch.bfloat16, device=dev)
+    cu = torch.zeros(1, dtype=torch.int32, device=dev)
+    tables = torch.empty(0, 1, dtype=torch.int32, device=dev)
+    out = nvpaged.nv_paged_attn_prefill(q, k, v, cu, cu, 0, 0, tables, shape.num_kv_heads,
+                                        shape.block_size, 0.088)
+    assert out.numel() == 0
+    lens = torch.empty(0, dtype=torch.int32, device=dev)
+    ws = torch.empty(1, dtype=torch.uint8, device=dev)
+    nvpaged.nv_paged_attn_decode(q, k, v, lens, tables, shape.num_kv_heads, shape.block_size,
+                                 0.088, workspace=ws, out=q)
+    nvpaged.nv_paged_attn_decode_noalloc(q, k, v, lens, tables, shape.num_kv_heads,
+                                         shape.block_size, 0.088, out=q)
+    nvpaged.nv_paged_attn_decode_store(q, key, key, slots, k, v, lens, tables,
+                                       shape.num_kv_heads, shape.block_size, 0.088,
+                                       workspace=ws, out=q)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(k), k0) and np.array_equal(bits(v), v0)

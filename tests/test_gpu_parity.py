@@ -52,7 +52,10 @@ SHAPES = [workloads.AttnShape(16, 8, 128, 256), workloads.AttnShape(32, 8, 128, 
           # these split each pair's heads into 3 units of 2 (G = 4) and 3 units of 1 (G = 7)
           workloads.AttnShape(24, 6, 128, 32), workloads.AttnShape(21, 3, 128, 64),
           # six query heads per kv head: decode_split_kernel<6, *> and two-head prefill groups
-          workloads.AttnShape(24, 4, 128, 256), workloads.AttnShape(12, 2, 128, 32)]
+          workloads.AttnShape(24, 4, 128, 256), workloads.AttnShape(12, 2, 128, 32),
+          # one-key blocks: every key its own table entry (decode splits capped by the table
+          # slice staged in LDS)
+          workloads.AttnShape(16, 8, 128, 1)]
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"{s.num_heads}q{s.num_kv_heads}kv_bs{s.block_size}")

@@ -47,7 +47,7 @@ extern "C" {
 typedef enum {
     NV_OK = 0,
     NV_ERR_INVALID_ARG = -1, /* null pointer, negative size, inconsistent shapes or strides */
-    NV_ERR_UNSUPPORTED = -2, /* valid request this build does not implement (e.g. head_dim) */
+    NV_ERR_UNSUPPORTED = -2, /* valid request this library does not implement (e.g. head_dim) */
     NV_ERR_LAUNCH = -3,      /* the HIP runtime rejected a kernel launch */
     NV_ERR_WORKSPACE = -4,   /* decode workspace missing or smaller than required */
     NV_ERR_SCRATCH = -5      /* the library's static scratch is smaller than the call needs */

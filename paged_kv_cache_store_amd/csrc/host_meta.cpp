@@ -11,7 +11,7 @@ extern "C" const char *nv_status_string(nv_status status) {
     switch (status) {
         case NV_OK: return "NV_OK";
         case NV_ERR_INVALID_ARG: return "NV_ERR_INVALID_ARG: invalid argument";
-        case NV_ERR_UNSUPPORTED: return "NV_ERR_UNSUPPORTED: shape not implemented by this build";
+        case NV_ERR_UNSUPPORTED: return "NV_ERR_UNSUPPORTED: shape not implemented by this library";
         case NV_ERR_LAUNCH: return "NV_ERR_LAUNCH: kernel launch failed";
         case NV_ERR_WORKSPACE: return "NV_ERR_WORKSPACE: decode workspace missing or too small";
         case NV_ERR_SCRATCH:

@@ -12,7 +12,7 @@
 namespace nvp {
 
 constexpr int kWave = 64;
-constexpr int kHeadDim = 128;  // the only head size this build implements
+constexpr int kHeadDim = 128;  // the only head size this library implements
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;

@@ -3,7 +3,9 @@ libnvprobe.so, the benchmark's measurement helper behind include/nv_probe.h (not
 paged-KV path).
 
 Every source is compiled for gfx950 only, with packed-fp32 instruction selection disabled, then
-linked into its shared library next to this file.
+linked into its shared library next to this file. The prefill source is scheduled with the
+backend's iterative ILP strategy (measured 1-4% faster than the default scheduler on every
+prefill workload, at the same register count and occupancy).
 """
 from __future__ import annotations
 
@@ -26,13 +28,15 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC,
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-function"]
+# Per-source additions.
+SOURCE_FLAGS = {"prefill.hip": ["-mllvm", "--amdgpu-sched-strategy=iterative-ilp"]}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, src + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    subprocess.run([HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj],
-                   check=True)
+    subprocess.run([HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), *lang, "-c",
+                    os.path.join(CSRC, src), "-o", obj], check=True)
     return obj
 
 

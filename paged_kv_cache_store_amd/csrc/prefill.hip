@@ -55,10 +55,12 @@
 #define NV_PREFILL_FASTCOPY 1  // whole-block tiles: scalar base address + fixed lane offsets
 #endif
 #ifndef NV_PREFILL_KPF
-#define NV_PREFILL_KPF 3       // K fragments read this many dim-steps ahead of their products
+#define NV_PREFILL_KPF 4       // K fragments read this many dim-steps ahead of their products
 #endif
+// Scheduling-group pins for the K read / score product interleave: off, since the iterative
+// ILP scheduler this file is built with orders the loop better unpinned.
 #ifndef NV_PREFILL_SGB
-#define NV_PREFILL_SGB 1       // pin the read/product interleave with scheduling group barriers
+#define NV_PREFILL_SGB 0
 #endif
 #ifndef NV_PREFILL_VPF
 #define NV_PREFILL_VPF 1       // read the first P.V step's V fragments before the softmax
